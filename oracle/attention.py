@@ -1,0 +1,129 @@
+"""Decode attention over a JoLT-compressed cache, and dense decode attention.
+
+"A JoLT for the KV cache" (arXiv 2607.12550v4 summary), Abstract and §4.5:
+the decode kernel evaluates attention directly over the stored factors and
+packed residuals; keys need full reconstruction because RoPE does not commute
+with the factorisation.  Whatever the kernel does, the value it computes is
+plain softmax attention of the RoPE'd query over the decoded cache, which is
+what this module writes out:
+
+  K^[l, h] = A_K G_K[l', h] B_K^T + [b_K > 0] deq(codes_K[l', h]) Pi^T  (V^ alike)
+  s_t      = scale * rope(q_j, q_pos) . rope(K^[l, h]_t, t)
+  p        = softmax(s)                (max-subtracted, float64)
+  o_j      = sum_t p_t V^[l, h]_t
+
+for query head j served by KV head h = floor(j / H_grp) (grouped-query
+attention: the sarnas.ru post's 70B example, 8 query heads per KV head), layer
+l in group g at index l' = l - group_start[g].  Readings taken: the query sits
+at position q_pos (normally T) and attends only to the T cached tokens; the
+output is float32-sized but computed here in float64.
+"""
+import numpy as np
+
+from .quant import dequantize, unpack
+from .rope import rope
+from .rotation import rotation
+
+
+def group_of(cache, layer):
+    gsl = cache["group_start"]
+    for g in range(len(gsl) - 1):
+        if gsl[g] <= layer < gsl[g + 1]:
+            return g, layer - gsl[g]
+    raise IndexError(layer)
+
+
+def residual(cell, lp, d):
+    """deq(codes) in the rotated basis for layer index lp: [H, T, d] or None."""
+    if cell["bits"] == 0:
+        return None
+    codes = unpack(cell["codes"][lp], cell["bits"], d)
+    return dequantize(codes, cell["scales"][lp], cell["bits"])
+
+
+def decode_cell(cell, lp, d, Pi):
+    """X^[lp] of one stored cell: [H, T, d] float64."""
+    A = cell["A"].astype(np.float64)
+    B = cell["B"].astype(np.float64)
+    G = cell["G"][lp].astype(np.float64)
+    H = G.shape[0]
+    T = A.shape[0]
+    out = np.zeros((H, T, d))
+    if cell["r_T"] > 0:
+        out += np.einsum("tr,hrs,fs->htf", A, G, B, optimize=True)
+    R = residual(cell, lp, d)
+    if R is not None:
+        out += R @ Pi.T
+    return out
+
+
+def softmax_attention(qr, Kr, V, scale):
+    """qr [Hg, d], Kr [T, d], V [T, d] -> [Hg, d] (float64)."""
+    s = scale * (qr @ Kr.T)
+    s = s - np.max(s, axis=-1, keepdims=True)
+    p = np.exp(s)
+    p /= np.sum(p, axis=-1, keepdims=True)
+    return p @ V
+
+
+def decode_layer(cache, layer, q, q_pos, inv_freq, scale, Pi=None, heads=None):
+    """One sequence, one layer: q [H_q, d] -> o [H_q, d] (rows of ``heads`` only
+    when a subset of KV heads is requested; other rows are NaN)."""
+    d, H, H_q, T = cache["d"], cache["H"], cache["H_q"], cache["T"]
+    if Pi is None:
+        Pi = rotation(cache["rotation_seed"], d)
+    g, lp = group_of(cache, layer)
+    cK, cV = cache["cells"][g]
+    Hg = H_q // H
+    heads = range(H) if heads is None else heads
+    qr = rope(np.asarray(q, dtype=np.float64), q_pos, inv_freq)
+    pos = np.arange(T)
+    out = np.full((H_q, d), np.nan)
+    Khat = decode_cell(cK, lp, d, Pi)
+    Vhat = decode_cell(cV, lp, d, Pi)
+    for h in heads:
+        Kr = rope(Khat[h], pos, inv_freq)
+        out[h * Hg:(h + 1) * Hg] = softmax_attention(qr[h * Hg:(h + 1) * Hg], Kr, Vhat[h], scale)
+    return out
+
+
+def decode_attention(caches, layer, q, q_pos, inv_freq, scale):
+    """Batch of sequences: q [B, H_q, d], q_pos [B] -> [B, H_q, d]."""
+    Pi_cache = {}
+    out = []
+    for b, c in enumerate(caches):
+        key = (c["rotation_seed"], c["d"])
+        if key not in Pi_cache:
+            Pi_cache[key] = rotation(*key)
+        out.append(decode_layer(c, layer, q[b], int(q_pos[b]), inv_freq, scale, Pi_cache[key]))
+    return np.stack(out)
+
+
+def factored_value_output(p, cellV, lp, h, d, Pi):
+    """The value path by linearity, never forming V^:
+    o = (p A_V) G_V[lp, h] B_V^T + (p deq_V[lp, h]) Pi^T  for p [Hg, T]."""
+    A = cellV["A"].astype(np.float64)
+    o = np.zeros((p.shape[0], d))
+    if cellV["r_T"] > 0:
+        a = p @ A
+        o += (a @ cellV["G"][lp, h].astype(np.float64)) @ cellV["B"].astype(np.float64).T
+    R = residual(cellV, lp, d)
+    if R is not None:
+        o += (p @ R[h]) @ Pi.T
+    return o
+
+
+def dense_attention(k_rope, v, q, q_pos, inv_freq, scale):
+    """Dense decode over post-RoPE keys: k_rope, v [B, H, T, d]; q [B, H_q, d]
+    (pre-RoPE; rotated to q_pos here) -> [B, H_q, d]."""
+    Bn, H, T, d = k_rope.shape
+    H_q = q.shape[1]
+    Hg = H_q // H
+    out = np.empty((Bn, H_q, d))
+    for b in range(Bn):
+        qr = rope(np.asarray(q[b], dtype=np.float64), int(q_pos[b]), inv_freq)
+        for h in range(H):
+            out[b, h * Hg:(h + 1) * Hg] = softmax_attention(
+                qr[h * Hg:(h + 1) * Hg], np.asarray(k_rope[b, h], dtype=np.float64),
+                np.asarray(v[b, h], dtype=np.float64), scale)
+    return out
