@@ -1,0 +1,602 @@
+// Host side of libjolt: argument validation, error reporting, cache upload
+// and re-layout, and kernel dispatch.  Every entry point is declared, with
+// its contract, in include/jolt.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "jolt.h"
+#include "jolt_internal.h"
+
+namespace jolt {
+void make_rotation(uint64_t seed, int d, double *out);
+}
+
+using namespace jolt;
+
+// ---------------------------------------------------------------- errors --
+static thread_local std::string g_err;
+
+static jolt_status fail(jolt_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+static jolt_status ok() {
+  g_err.clear();
+  return JOLT_OK;
+}
+
+#define HIP_TRY(expr)                                                               \
+  do {                                                                              \
+    hipError_t e_ = (expr);                                                         \
+    if (e_ != hipSuccess) return fail(JOLT_E_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+extern "C" const char *jolt_last_error(void) { return g_err.c_str(); }
+
+// ------------------------------------------------------------- helpers --
+static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static inline float bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// --------------------------------------------------------- cache handle --
+struct CellMeta {
+  int rT, rF, bits, rT_pad, rF_pad, kw;
+};
+
+struct jolt_cache {
+  int n_layers = 0, n_groups = 0, H = 0, H_q = 0, d = 0, T = 0, T_pad = 0;
+  bool f32 = false;
+  int device = 0;
+  std::vector<int> group_start;
+  std::vector<CellMeta> cells;      // [n_groups * 2]
+  std::vector<int> layer_group;     // [n_layers]
+  void *dev = nullptr;
+  size_t dev_bytes = 0;
+  LayerDev *d_layers = nullptr;     // inside dev
+  std::vector<LayerDev> h_layers;   // host mirror of d_layers
+};
+
+// ---------------------------------------------------------- validation --
+static jolt_status validate_desc(const jolt_cache_desc *d) {
+  if (!d) return fail(JOLT_E_INVALID, "desc is NULL");
+  if (d->n_layers < 1 || d->n_groups < 1 || d->n_groups > d->n_layers)
+    return fail(JOLT_E_INVALID, "n_layers=%d n_groups=%d", d->n_layers, d->n_groups);
+  if (d->n_kv_heads < 1 || d->n_q_heads < 1 || d->n_q_heads % d->n_kv_heads)
+    return fail(JOLT_E_INVALID, "n_q_heads=%d must be a positive multiple of n_kv_heads=%d",
+                d->n_q_heads, d->n_kv_heads);
+  if (d->head_dim < 2 || d->head_dim % 2)
+    return fail(JOLT_E_INVALID, "head_dim=%d must be even", d->head_dim);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(JOLT_E_UNSUPPORTED, "head_dim=%d: supported 64, 128", d->head_dim);
+  if (d->n_q_heads / d->n_kv_heads > kMaxHg)
+    return fail(JOLT_E_UNSUPPORTED, "query heads per KV head %d > %d",
+                d->n_q_heads / d->n_kv_heads, kMaxHg);
+  if (d->T < 1) return fail(JOLT_E_INVALID, "T=%d must be >= 1", d->T);
+  if ((int64_t)d->T > (1 << 24)) return fail(JOLT_E_UNSUPPORTED, "T=%d too large", d->T);
+  if (d->factor_dtype != JOLT_F32 && d->factor_dtype != JOLT_BF16)
+    return fail(JOLT_E_INVALID, "factor_dtype=%d", (int)d->factor_dtype);
+  if (!d->group_start || !d->cells) return fail(JOLT_E_INVALID, "group_start or cells is NULL");
+  if (d->group_start[0] != 0 || d->group_start[d->n_groups] != d->n_layers)
+    return fail(JOLT_E_INVALID, "group_start must run from 0 to n_layers");
+  for (int g = 0; g < d->n_groups; ++g)
+    if (d->group_start[g + 1] <= d->group_start[g])
+      return fail(JOLT_E_INVALID, "group_start not strictly increasing at %d", g);
+  for (int g = 0; g < d->n_groups; ++g) {
+    int gs = d->group_start[g + 1] - d->group_start[g];
+    int64_t rmax = std::min<int64_t>(d->T, (int64_t)gs * d->n_kv_heads * d->head_dim);
+    for (int tau = 0; tau < 2; ++tau) {
+      const jolt_cell &c = d->cells[2 * g + tau];
+      if (c.r_T < 0 || c.r_T > rmax || c.r_F < 0 || c.r_F > d->head_dim)
+        return fail(JOLT_E_INVALID, "cell (%d,%d): r_T=%d (max %lld), r_F=%d (max %d)", g, tau,
+                    c.r_T, (long long)rmax, c.r_F, d->head_dim);
+      if ((c.r_T == 0) != (c.r_F == 0))
+        return fail(JOLT_E_INVALID, "cell (%d,%d): r_T=%d and r_F=%d must be zero together", g,
+                    tau, c.r_T, c.r_F);
+      if (c.bits != 0 && c.bits != 2 && c.bits != 4 && c.bits != 8)
+        return fail(JOLT_E_INVALID, "cell (%d,%d): bits=%d not in {0,2,4,8}", g, tau, c.bits);
+      if (c.r_T > 0 && (!c.A || !c.B || !c.G))
+        return fail(JOLT_E_INVALID, "cell (%d,%d): A, B, G required when r_T > 0", g, tau);
+      if ((c.bits > 0) != (c.codes != nullptr) || (c.bits > 0) != (c.scales != nullptr))
+        return fail(JOLT_E_INVALID, "cell (%d,%d): codes/scales must be non-NULL iff bits > 0",
+                    g, tau);
+    }
+  }
+  return JOLT_OK;
+}
+
+// ------------------------------------------------------- layout builder --
+// One host staging buffer mirrors the single device allocation.
+struct Staging {
+  std::vector<uint8_t> buf;
+  size_t take(size_t bytes) {
+    size_t off = buf.size();
+    buf.resize(off + align256(bytes), 0);
+    return off;
+  }
+};
+
+static float load_factor(const void *p, size_t i, bool f32) {
+  return f32 ? ((const float *)p)[i] : bf16_to_f32(((const uint16_t *)p)[i]);
+}
+static void store_factor(uint8_t *dst, size_t i, const void *src, size_t j, bool f32) {
+  if (f32)
+    ((float *)dst)[i] = ((const float *)src)[j];
+  else
+    ((uint16_t *)dst)[i] = ((const uint16_t *)src)[j];
+}
+
+static inline int canon_code(const uint8_t *row, int i, int bits) {
+  int per = 8 / bits;
+  return (row[i / per] >> ((i % per) * bits)) & ((1 << bits) - 1);
+}
+
+extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream stream,
+                                       jolt_cache **out) {
+  if (!out) return fail(JOLT_E_INVALID, "out is NULL");
+  *out = nullptr;
+  jolt_status st = validate_desc(desc);
+  if (st != JOLT_OK) return st;
+  const char *fa = std::getenv("JOLT_TEST_FAIL_ALLOC");
+  if (fa && fa[0] == '1') return fail(JOLT_E_OOM, "allocation failure forced by JOLT_TEST_FAIL_ALLOC");
+
+  jolt_cache *c = new (std::nothrow) jolt_cache();
+  if (!c) return fail(JOLT_E_OOM, "host allocation failed");
+  const int H = desc->n_kv_heads, d = desc->head_dim, T = desc->T;
+  const bool f32 = desc->factor_dtype == JOLT_F32;
+  const int fb = f32 ? 4 : 2;
+  c->n_layers = desc->n_layers;
+  c->n_groups = desc->n_groups;
+  c->H = H;
+  c->H_q = desc->n_q_heads;
+  c->d = d;
+  c->T = T;
+  c->T_pad = round_up(T, kTokPad);
+  c->f32 = f32;
+  c->group_start.assign(desc->group_start, desc->group_start + desc->n_groups + 1);
+  c->layer_group.resize(c->n_layers);
+  for (int g = 0; g < c->n_groups; ++g)
+    for (int l = c->group_start[g]; l < c->group_start[g + 1]; ++l) c->layer_group[l] = g;
+  const int T_pad = c->T_pad;
+
+  std::vector<double> Pi64((size_t)d * d);
+  make_rotation(desc->rotation_seed, d, Pi64.data());
+
+  Staging S;
+  try {
+    size_t off_pi = S.take(sizeof(float) * d * d);
+    for (int i = 0; i < d * d; ++i) ((float *)(S.buf.data() + off_pi))[i] = (float)Pi64[i];
+
+    struct Offs {
+      size_t A, B, W;
+      std::vector<size_t> G, codes, scales;  // per layer in group
+    };
+    std::vector<Offs> offs(2 * c->n_groups);
+    c->cells.resize(2 * c->n_groups);
+    for (int g = 0; g < c->n_groups; ++g) {
+      const int gs = c->group_start[g + 1] - c->group_start[g];
+      for (int tau = 0; tau < 2; ++tau) {
+        const jolt_cell &in = desc->cells[2 * g + tau];
+        CellMeta m;
+        m.rT = in.r_T;
+        m.rF = in.r_F;
+        m.bits = in.bits;
+        m.rT_pad = round_up(in.r_T, kRankPad);
+        m.rF_pad = round_up(in.r_F, kRankPad);
+        m.kw = m.rF_pad + (in.bits > 0 ? d : 0);
+        c->cells[2 * g + tau] = m;
+        Offs &o = offs[2 * g + tau];
+        // A
+        o.A = S.take((size_t)fb * T_pad * std::max(m.rT_pad, 1));
+        for (int t = 0; t < T; ++t)
+          for (int r = 0; r < m.rT; ++r) {
+            size_t dst = tau == 0 ? (size_t)t * m.rT_pad + r
+                                  : (size_t)r * T_pad + (t & ~31) + perm32_inv(t & 31);
+            store_factor(S.buf.data() + o.A, dst, in.A, (size_t)t * m.rT + r, f32);
+          }
+        // B
+        o.B = S.take((size_t)fb * d * std::max(m.rF_pad, 1));
+        for (int f = 0; f < d; ++f)
+          for (int j = 0; j < m.rF; ++j)
+            store_factor(S.buf.data() + o.B, (size_t)f * m.rF_pad + j, in.B, (size_t)f * m.rF + j,
+                         f32);
+        // W = [B_K (slot-permuted) | Pi] in fp16, keys of bf16 caches only
+        o.W = 0;
+        if (tau == 0 && !f32) {
+          o.W = S.take(sizeof(_Float16) * d * m.kw);
+          _Float16 *W = (_Float16 *)(S.buf.data() + o.W);
+          for (int f = 0; f < d; ++f) {
+            for (int col = 0; col < m.rF_pad; ++col) {
+              int j = (col & ~31) + perm32(col & 31);
+              float v = j < m.rF ? load_factor(in.B, (size_t)f * m.rF + j, false) : 0.0f;
+              W[(size_t)f * m.kw + col] = (_Float16)v;
+            }
+            if (m.bits > 0)
+              for (int i = 0; i < d; ++i)
+                W[(size_t)f * m.kw + m.rF_pad + i] = (_Float16)Pi64[(size_t)f * d + i];
+          }
+        }
+        // G and residual, per layer of the group
+        for (int lp = 0; lp < gs; ++lp) {
+          size_t og = S.take((size_t)fb * H * std::max(m.rT_pad, 1) * std::max(m.rF_pad, 1));
+          o.G.push_back(og);
+          for (int h = 0; h < H; ++h)
+            for (int r = 0; r < m.rT; ++r)
+              for (int j = 0; j < m.rF; ++j) {
+                size_t src = (((size_t)lp * H + h) * m.rT + r) * m.rF + j;
+                size_t dst = tau == 0 ? ((size_t)h * m.rF_pad + j) * m.rT_pad + r
+                                      : ((size_t)h * m.rT_pad + r) * m.rF_pad + j;
+                store_factor(S.buf.data() + og, dst, in.G, src, f32);
+              }
+          if (m.bits == 0) {
+            o.codes.push_back(0);
+            o.scales.push_back(0);
+            continue;
+          }
+          const int b = m.bits, rowb = d * b / 8;
+          size_t oc = S.take((size_t)H * T_pad * rowb);
+          size_t os = S.take(sizeof(float) * H * T_pad);
+          o.codes.push_back(oc);
+          o.scales.push_back(os);
+          uint8_t *C = S.buf.data() + oc;
+          float *Sc = (float *)(S.buf.data() + os);
+          for (int h = 0; h < H; ++h)
+            for (int t = 0; t < T; ++t) {
+              const uint8_t *row = in.codes + (((size_t)lp * H + h) * T + t) * rowb;
+              Sc[(size_t)h * T_pad + t] = in.scales[((size_t)lp * H + h) * T + t];
+              for (int i = 0; i < d; ++i) {
+                uint32_t code = (uint32_t)canon_code(row, i, b);
+                int dw, sh;
+                if (tau == 0) {
+                  int s = i >> 5, g2 = (i >> 3) & 3, j = i & 7;
+                  code_pos(8 * s + j, b, &dw, &sh);
+                  uint32_t *w = (uint32_t *)(C + ((size_t)h * T_pad + t) * rowb + g2 * (d * b / 32));
+                  w[dw] |= code << sh;
+                } else {
+                  code_pos(perm32_inv(t & 31), b, &dw, &sh);
+                  uint32_t *w = (uint32_t *)(C + (((size_t)h * (T_pad / 32) + t / 32) * d + i) * (4 * b));
+                  w[dw] |= code << sh;
+                }
+              }
+            }
+        }
+      }
+    }
+    size_t off_layers = S.take(sizeof(LayerDev) * c->n_layers);
+    c->dev_bytes = S.buf.size();
+    hipError_t e = hipMalloc(&c->dev, c->dev_bytes);
+    if (e != hipSuccess) {
+      delete c;
+      return fail(e == hipErrorOutOfMemory ? JOLT_E_OOM : JOLT_E_HIP, "hipMalloc(%zu): %s",
+                  S.buf.size(), hipGetErrorString(e));
+    }
+    hipGetDevice(&c->device);
+    uint8_t *base = (uint8_t *)c->dev;
+    c->h_layers.resize(c->n_layers);
+    for (int l = 0; l < c->n_layers; ++l) {
+      const int g = c->layer_group[l], lp = l - c->group_start[g];
+      LayerDev &L = c->h_layers[l];
+      std::memset(&L, 0, sizeof L);
+      L.Pi = (const float *)(base + off_pi);
+      L.T = T;
+      L.T_pad = T_pad;
+      L.f32 = f32 ? 1 : 0;
+      for (int tau = 0; tau < 2; ++tau) {
+        const CellMeta &m = c->cells[2 * g + tau];
+        const Offs &o = offs[2 * g + tau];
+        CellDev &cd = L.c[tau];
+        cd.A = base + o.A;
+        cd.B = base + o.B;
+        cd.G = base + o.G[lp];
+        cd.W = o.W ? (const _Float16 *)(base + o.W) : nullptr;
+        cd.codes = m.bits ? base + o.codes[lp] : nullptr;
+        cd.scales = m.bits ? (const float *)(base + o.scales[lp]) : nullptr;
+        cd.rT = m.rT;
+        cd.rF = m.rF;
+        cd.bits = m.bits;
+        cd.rT_pad = m.rT_pad;
+        cd.rF_pad = m.rF_pad;
+        cd.kw = m.kw;
+      }
+    }
+    std::memcpy(S.buf.data() + off_layers, c->h_layers.data(), sizeof(LayerDev) * c->n_layers);
+    c->d_layers = (LayerDev *)(base + off_layers);
+    hipStream_t s = (hipStream_t)stream;
+    e = hipMemcpyAsync(c->dev, S.buf.data(), S.buf.size(), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      hipFree(c->dev);
+      delete c;
+      return fail(JOLT_E_HIP, "upload: %s", hipGetErrorString(e));
+    }
+  } catch (const std::bad_alloc &) {
+    if (c->dev) hipFree(c->dev);
+    delete c;
+    return fail(JOLT_E_OOM, "host staging allocation failed");
+  }
+  *out = c;
+  return ok();
+}
+
+extern "C" jolt_status jolt_free_cache(jolt_cache *c) {
+  if (!c) return ok();
+  hipError_t e = c->dev ? hipFree(c->dev) : hipSuccess;
+  delete c;
+  if (e != hipSuccess) return fail(JOLT_E_HIP, "hipFree: %s", hipGetErrorString(e));
+  return ok();
+}
+
+extern "C" jolt_status jolt_cache_info(const jolt_cache *c, int32_t *n_layers, int32_t *n_kv,
+                                       int32_t *n_q, int32_t *d, int32_t *T, size_t *bytes) {
+  if (!c) return fail(JOLT_E_INVALID, "cache is NULL");
+  if (n_layers) *n_layers = c->n_layers;
+  if (n_kv) *n_kv = c->H;
+  if (n_q) *n_q = c->H_q;
+  if (d) *d = c->d;
+  if (T) *T = c->T;
+  if (bytes) *bytes = c->dev_bytes;
+  return ok();
+}
+
+// ------------------------------------------------------- decode planning --
+struct Plan {
+  int kernel;        // JOLT_KERNEL_GENERIC or JOLT_KERNEL_MFMA
+  int split_tokens, n_split, rV_max, stride, T_max;
+  int lds_bytes;     // MFMA only
+  size_t ws_bytes;
+};
+
+static bool mfma_ok(const jolt_cache *c, int layer, int *lds) {
+  if (c->f32 || c->d != 128) return false;
+  const LayerDev &L = c->h_layers[layer];
+  const CellDev &k = L.c[0], &v = L.c[1];
+  if (v.rT_pad > 1024 || k.rT_pad > 1024) return false;
+  int bytes = 2 * k.rF_pad * k.rT_pad + 2 * c->d * k.kw + 32768;
+  *lds = bytes;
+  return bytes <= jolt_mfma_max_lds();
+}
+
+static jolt_status plan_decode(const jolt_cache *const *caches, int batch, int layer,
+                               const jolt_launch *launch, Plan *p) {
+  if (batch < 0) return fail(JOLT_E_INVALID, "batch=%d", batch);
+  if (batch > 0 && !caches) return fail(JOLT_E_INVALID, "caches is NULL");
+  const jolt_cache *c0 = batch ? caches[0] : nullptr;
+  for (int b = 0; b < batch; ++b) {
+    const jolt_cache *c = caches[b];
+    if (!c) return fail(JOLT_E_INVALID, "caches[%d] is NULL", b);
+    if (c->n_layers != c0->n_layers || c->H != c0->H || c->H_q != c0->H_q || c->d != c0->d ||
+        c->group_start != c0->group_start || c->f32 != c0->f32)
+      return fail(JOLT_E_INVALID,
+                  "caches[%d] differs in layers, groups, heads, head_dim or factor dtype", b);
+  }
+  if (batch && (layer < 0 || layer >= c0->n_layers))
+    return fail(JOLT_E_INVALID, "layer=%d out of range [0,%d)", layer, c0->n_layers);
+  int want = launch ? launch->kernel : JOLT_KERNEL_AUTO;
+  if (want < 0 || want > 2) return fail(JOLT_E_INVALID, "launch->kernel=%d", want);
+  if (launch && launch->split_tokens < 0)
+    return fail(JOLT_E_INVALID, "launch->split_tokens=%d", launch->split_tokens);
+  p->T_max = 1;
+  p->rV_max = 0;
+  bool mf = batch > 0;
+  p->lds_bytes = 0;
+  for (int b = 0; b < batch; ++b) {
+    const jolt_cache *c = caches[b];
+    p->T_max = std::max(p->T_max, c->T);
+    p->rV_max = std::max(p->rV_max, c->h_layers[layer].c[1].rT_pad);
+    int lds = 0;
+    if (!mfma_ok(c, layer, &lds)) mf = false;
+    p->lds_bytes = std::max(p->lds_bytes, lds);
+  }
+  if (want == JOLT_KERNEL_MFMA && !mf)
+    return fail(JOLT_E_UNSUPPORTED,
+                "MFMA kernel needs bf16 factors, d=128, ranks <= 1024 and an LDS fit");
+  p->kernel = (want == JOLT_KERNEL_GENERIC || !mf) ? JOLT_KERNEL_GENERIC : JOLT_KERNEL_MFMA;
+  const int tile = p->kernel == JOLT_KERNEL_MFMA ? kTokPad : 32;
+  int H = batch ? c0->H : 1;
+  int split = launch && launch->split_tokens > 0 ? launch->split_tokens : 0;
+  if (split == 0) {
+    int want_wg = 512;
+    int n = std::max(1, (want_wg + batch * H - 1) / std::max(1, batch * H));
+    split = (p->T_max + n - 1) / n;
+  }
+  p->split_tokens = round_up(std::max(split, 1), tile);
+  p->split_tokens = std::max(p->split_tokens, round_up((p->T_max + kMaxSplits - 1) / kMaxSplits, tile));
+  p->n_split = (p->T_max + p->split_tokens - 1) / p->split_tokens;
+  p->stride = partial_stride(p->rV_max, batch ? c0->d : 0);
+  p->ws_bytes = (size_t)batch * (batch ? c0->H_q : 0) * p->n_split * p->stride * sizeof(float);
+  return JOLT_OK;
+}
+
+extern "C" jolt_status jolt_decode_workspace_size(const jolt_cache *const *caches, int32_t batch,
+                                                  int32_t layer, const jolt_launch *launch,
+                                                  size_t *bytes) {
+  if (!bytes) return fail(JOLT_E_INVALID, "bytes is NULL");
+  Plan p;
+  jolt_status st = plan_decode(caches, batch, layer, launch, &p);
+  if (st != JOLT_OK) return st;
+  *bytes = p.ws_bytes;
+  return ok();
+}
+
+extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, int32_t batch,
+                                             int32_t layer, const void *q, jolt_dtype q_dtype,
+                                             const int32_t *q_pos, const float *inv_freq,
+                                             float softmax_scale, float *out, void *workspace,
+                                             size_t ws_bytes, const jolt_launch *launch,
+                                             jolt_stream stream) {
+  Plan p;
+  jolt_status st = plan_decode(caches, batch, layer, launch, &p);
+  if (st != JOLT_OK) return st;
+  if (batch == 0) return ok();
+  if (!q || !q_pos || !inv_freq || !out) return fail(JOLT_E_INVALID, "NULL q/q_pos/inv_freq/out");
+  if (q_dtype != JOLT_F32 && q_dtype != JOLT_BF16) return fail(JOLT_E_INVALID, "q_dtype");
+  if (!std::isfinite(softmax_scale)) return fail(JOLT_E_INVALID, "softmax_scale not finite");
+  for (int b = 0; b < batch; ++b)
+    if (q_pos[b] < 0) return fail(JOLT_E_INVALID, "q_pos[%d]=%d < 0", b, q_pos[b]);
+  if (!workspace || ws_bytes < p.ws_bytes)
+    return fail(JOLT_E_WORKSPACE, "workspace %zu bytes, need %zu", workspace ? ws_bytes : 0,
+                p.ws_bytes);
+  const jolt_cache *c0 = caches[0];
+  hipStream_t s = (hipStream_t)stream;
+  DecodeArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.scale = softmax_scale;
+  a.q_f32 = q_dtype == JOLT_F32;
+  a.f32 = c0->f32 ? 1 : 0;
+  a.H = c0->H;
+  a.H_q = c0->H_q;
+  a.Hg = c0->H_q / c0->H;
+  a.d = c0->d;
+  for (int i = 0; i < c0->d / 2; ++i) a.inv_freq[i] = inv_freq[i];
+  a.n_split = p.n_split;
+  a.split_tokens = p.split_tokens;
+  a.stride = p.stride;
+  a.rV_max = p.rV_max;
+  const size_t qbytes = (size_t)c0->H_q * c0->d * (a.q_f32 ? 4 : 2);
+  for (int b0 = 0; b0 < batch; b0 += kMaxBatchPerLaunch) {
+    int nb = std::min(kMaxBatchPerLaunch, batch - b0);
+    a.q = (const uint8_t *)q + b0 * qbytes;
+    a.out = out + (size_t)b0 * c0->H_q * c0->d;
+    a.ws = (float *)workspace + (size_t)b0 * c0->H_q * p.n_split * p.stride;
+    a.nseq = nb;
+    for (int i = 0; i < nb; ++i) {
+      a.seq[i].layer = caches[b0 + i]->d_layers + layer;
+      a.seq[i].q_pos = q_pos[b0 + i];
+      a.seq[i].T = caches[b0 + i]->T;
+    }
+    hipError_t e = p.kernel == JOLT_KERNEL_MFMA
+                       ? jolt_launch_mfma(a, nb, caches[b0]->h_layers[layer].c[0].bits,
+                                          caches[b0]->h_layers[layer].c[1].bits, p.lds_bytes, s)
+                       : jolt_launch_generic(a, nb, s);
+    if (e != hipSuccess) return fail(JOLT_E_HIP, "split kernel launch: %s", hipGetErrorString(e));
+    e = jolt_launch_merge(a, nb, s);
+    if (e != hipSuccess) return fail(JOLT_E_HIP, "merge kernel launch: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+// ----------------------------------------------------------------- dense --
+static jolt_status plan_dense(int batch, int n_kv, int n_q, int d, int T, const jolt_launch *launch,
+                              int *split_tokens, int *n_split, size_t *bytes) {
+  if (batch < 0 || n_kv < 1 || n_q < 1 || T < 1 || n_q % n_kv)
+    return fail(JOLT_E_INVALID, "batch=%d n_kv=%d n_q=%d T=%d", batch, n_kv, n_q, T);
+  if (d != 64 && d != 128) return fail(JOLT_E_UNSUPPORTED, "d=%d: supported 64, 128", d);
+  if (n_q / n_kv > kMaxHg) return fail(JOLT_E_UNSUPPORTED, "n_q/n_kv > %d", kMaxHg);
+  if (launch && launch->split_tokens < 0) return fail(JOLT_E_INVALID, "split_tokens < 0");
+  int split = launch && launch->split_tokens > 0 ? launch->split_tokens : 0;
+  if (split == 0) {
+    int n = std::max(1, (1024 + batch * n_kv - 1) / std::max(1, batch * n_kv));
+    split = (T + n - 1) / n;
+  }
+  *split_tokens = round_up(std::max(split, 1), 64);
+  *n_split = (T + *split_tokens - 1) / *split_tokens;
+  *bytes = (size_t)batch * n_q * *n_split * (4 + d) * sizeof(float);
+  return JOLT_OK;
+}
+
+extern "C" jolt_status jolt_dense_workspace_size(int32_t batch, int32_t n_kv, int32_t n_q,
+                                                 int32_t d, int32_t T, const jolt_launch *launch,
+                                                 size_t *bytes) {
+  if (!bytes) return fail(JOLT_E_INVALID, "bytes is NULL");
+  int st_, ns;
+  jolt_status st = plan_dense(batch, n_kv, n_q, d, T, launch, &st_, &ns, bytes);
+  return st == JOLT_OK ? ok() : st;
+}
+
+extern "C" jolt_status jolt_dense_attention(const void *k_rope, const void *v, jolt_dtype kv_dtype,
+                                            int32_t batch, int32_t n_kv, int32_t n_q, int32_t d,
+                                            int32_t T, const void *q, jolt_dtype q_dtype,
+                                            const int32_t *q_pos, const float *inv_freq,
+                                            float softmax_scale, float *out, void *workspace,
+                                            size_t ws_bytes, const jolt_launch *launch,
+                                            jolt_stream stream) {
+  int split_tokens, n_split;
+  size_t need;
+  jolt_status st = plan_dense(batch, n_kv, n_q, d, T, launch, &split_tokens, &n_split, &need);
+  if (st != JOLT_OK) return st;
+  if (batch == 0) return ok();
+  if (!k_rope || !v || !q || !q_pos || !inv_freq || !out)
+    return fail(JOLT_E_INVALID, "NULL pointer argument");
+  if ((kv_dtype != JOLT_F32 && kv_dtype != JOLT_BF16) || (q_dtype != JOLT_F32 && q_dtype != JOLT_BF16))
+    return fail(JOLT_E_INVALID, "dtype");
+  if (!std::isfinite(softmax_scale)) return fail(JOLT_E_INVALID, "softmax_scale not finite");
+  for (int b = 0; b < batch; ++b)
+    if (q_pos[b] < 0) return fail(JOLT_E_INVALID, "q_pos[%d]=%d < 0", b, q_pos[b]);
+  if (!workspace || ws_bytes < need)
+    return fail(JOLT_E_WORKSPACE, "workspace %zu bytes, need %zu", workspace ? ws_bytes : 0, need);
+  DenseArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.scale = softmax_scale;
+  a.kv_f32 = kv_dtype == JOLT_F32;
+  a.q_f32 = q_dtype == JOLT_F32;
+  a.H = n_kv;
+  a.H_q = n_q;
+  a.Hg = n_q / n_kv;
+  a.d = d;
+  a.T = T;
+  a.n_split = n_split;
+  a.split_tokens = split_tokens;
+  for (int i = 0; i < d / 2; ++i) a.inv_freq[i] = inv_freq[i];
+  const size_t kvb = (size_t)n_kv * T * d * (a.kv_f32 ? 4 : 2);
+  const size_t qb = (size_t)n_q * d * (a.q_f32 ? 4 : 2);
+  hipStream_t s = (hipStream_t)stream;
+  for (int b0 = 0; b0 < batch; b0 += kMaxBatchPerLaunch) {
+    int nb = std::min(kMaxBatchPerLaunch, batch - b0);
+    a.k = (const uint8_t *)k_rope + b0 * kvb;
+    a.v = (const uint8_t *)v + b0 * kvb;
+    a.q = (const uint8_t *)q + b0 * qb;
+    a.out = out + (size_t)b0 * n_q * d;
+    a.ws = (float *)workspace + (size_t)b0 * n_q * n_split * (4 + d);
+    a.batch = nb;
+    a.seq0 = b0;
+    for (int i = 0; i < nb; ++i) a.q_pos[i] = q_pos[b0 + i];
+    hipError_t e = jolt_launch_dense(a, nb, s);
+    if (e != hipSuccess) return fail(JOLT_E_HIP, "dense launch: %s", hipGetErrorString(e));
+    e = jolt_launch_dense_merge(a, nb, s);
+    if (e != hipSuccess) return fail(JOLT_E_HIP, "dense merge launch: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+// --------------------------------------------------------- test helpers --
+extern "C" jolt_status jolt_make_rotation(uint64_t seed, int32_t d, double *out) {
+  if (!out || d < 1 || d > 4096) return fail(JOLT_E_INVALID, "out NULL or d=%d", d);
+  jolt::make_rotation(seed, d, out);
+  return ok();
+}
+
+extern "C" jolt_status jolt_debug_unpack(const jolt_cache *c, int32_t layer, int32_t tau,
+                                         uint8_t *codes_out, jolt_stream stream) {
+  if (!c || !codes_out) return fail(JOLT_E_INVALID, "NULL argument");
+  if (layer < 0 || layer >= c->n_layers || (tau != 0 && tau != 1))
+    return fail(JOLT_E_INVALID, "layer=%d tau=%d", layer, tau);
+  if (c->h_layers[layer].c[tau].bits == 0) return fail(JOLT_E_INVALID, "cell has bits == 0");
+  hipStream_t s = (hipStream_t)stream;
+  size_t n = (size_t)c->H * c->T * c->d;
+  uint8_t *dbuf = nullptr;
+  HIP_TRY(hipMalloc(&dbuf, n));
+  hipError_t e = jolt_launch_unpack(c->d_layers + layer, tau, c->H, c->T, c->d, dbuf, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(codes_out, dbuf, n, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  hipFree(dbuf);
+  if (e != hipSuccess) return fail(JOLT_E_HIP, "debug unpack: %s", hipGetErrorString(e));
+  return ok();
+}

@@ -1,0 +1,128 @@
+// Internal types shared by the host code and the HIP kernels of libjolt.
+//
+// Device layout of a loaded cache (private; chosen for gfx950 MFMA operand
+// fragments, see the comments on each field).  Notation: H KV heads, d head
+// dim, T tokens, T_pad = T rounded up to 128, ranks padded to multiples of 32
+// with zeros (a zero rank column contributes nothing to any product).
+#pragma once
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "jolt.h"
+
+namespace jolt {
+
+constexpr int kTokPad = 128;    // T padding: one MFMA workgroup tile
+constexpr int kRankPad = 32;    // rank padding: one 16x16x32 MFMA K-step
+constexpr int kMaxHg = 16;      // query heads per KV head
+constexpr int kMaxBatchPerLaunch = 32;
+constexpr int kMaxD = 128;
+constexpr int kMaxSplits = 2048;
+
+// Token order inside each 32-token block of the value-path layouts: slot
+// q = 8g + j (g = 16-lane group, j = element of the 8-wide operand) holds
+// token perm32(q).  It is the order in which a 16x16 MFMA result tile (lane
+// group g holds rows 4g..4g+3) is re-read as the 32-deep K operand of the next
+// MFMA, so score tiles feed the value products without a transpose.
+__host__ __device__ inline int perm32(int q) {
+  int g = q >> 3, j = q & 7;
+  return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
+}
+__host__ __device__ inline int perm32_inv(int t) {
+  if (t < 16) return 8 * (t >> 2) + (t & 3);
+  t -= 16;
+  return 8 * (t >> 2) + 4 + (t & 3);
+}
+
+// Packed-code position of slot q (0..31 within one 32-slot group) for b bits:
+// dword q/2/(16/b), bit offset b*((q/2)%(16/b) + (q&1)*(16/b)).  With this
+// order one shift and one mask by (2^b-1)|(2^b-1)<<16 place two consecutive
+// slots in the two halves of a 32-bit word (two fp16 lanes).
+__host__ __device__ inline void code_pos(int q, int bits, int *dword, int *shift) {
+  int npair = 16 / bits;
+  int P = q >> 1;
+  *dword = P / npair;
+  *shift = bits * ((P % npair) + (q & 1) * npair);
+}
+
+struct CellDev {
+  // K: A [T_pad][rT_pad] row-major.
+  // V: A^T [rT_pad][T_pad], tokens in perm32 order inside 32-token blocks.
+  const void *A;
+  // K: G^T of this layer, [H][rF_pad][rT_pad].  V: G of this layer,
+  // [H][rT_pad][rF_pad].
+  const void *G;
+  const void *B;          // [d][rF_pad], factor dtype
+  const _Float16 *W;      // K, bf16 caches: [d][kw] fp16 = [B_K | Pi] (see host)
+  // Residual codes of this layer.
+  // K: [H][T_pad][d*b/8]; a row is 4 chunks (one per 16-lane group g) of
+  //    d*b/32 bytes; chunk g holds rotated features i = 32s + 8g + j as slot
+  //    q = 8s + j in code_pos order.
+  // V: [H][T_pad/32][d][4*b]: per (32-token block, feature) the 32 codes of
+  //    slots q = 0..31 (token perm32(q)) in code_pos order.
+  const uint8_t *codes;
+  const float *scales;    // this layer: [H][T_pad]
+  int32_t rT, rF, bits, rT_pad, rF_pad, kw;
+};
+
+struct LayerDev {
+  CellDev c[2];           // [0] = K, [1] = V
+  const float *Pi;        // [d][d] float32, row-major
+  int32_t T, T_pad, f32;  // f32: factors stored as float32 (else bf16)
+};
+
+struct SeqArg {
+  const LayerDev *layer;  // device pointer to this sequence's layer descriptor
+  int32_t q_pos;
+  int32_t T;
+};
+
+// Kernel arguments of one split-T launch (passed by value, < 4 KiB).
+struct DecodeArgs {
+  const void *q;          // [batch][H_q][d]
+  float *out;             // [batch][H_q][d]
+  float *ws;              // partials [batch][H_q][n_split][stride]
+  float inv_freq[kMaxD / 2];
+  float scale;
+  int32_t q_f32, f32;     // f32: the caches store float32 factors
+  int32_t H, H_q, Hg, d;
+  int32_t n_split, split_tokens, stride, rV_max;
+  int32_t nseq;
+  SeqArg seq[kMaxBatchPerLaunch];
+};
+
+// A partial is [m, l, 0, 0, a[rV_max], c[d]] (floats); m = -inf, l = 0 for
+// an empty split.
+__host__ __device__ inline int partial_stride(int rV_max, int d) {
+  int s = 4 + rV_max + d;
+  return (s + 3) & ~3;
+}
+
+struct DenseArgs {
+  const void *k;          // [batch][H][T][d]
+  const void *v;
+  const void *q;
+  float *out;
+  float *ws;              // [batch][H_q][n_split][4 + d]
+  float inv_freq[kMaxD / 2];
+  float scale;
+  int32_t kv_f32, q_f32;
+  int32_t batch, H, H_q, Hg, d, T;
+  int32_t n_split, split_tokens;
+  int32_t q_pos[kMaxBatchPerLaunch];
+  int32_t seq0;           // first sequence of this launch
+};
+
+}  // namespace jolt
+
+// Kernel launchers (kernels_*.hip).  Each returns the hipError_t of its launch.
+hipError_t jolt_launch_generic(const jolt::DecodeArgs &a, int nseq, hipStream_t s);
+hipError_t jolt_launch_mfma(const jolt::DecodeArgs &a, int nseq, int bK, int bV, int lds_bytes,
+                            hipStream_t s);
+hipError_t jolt_launch_merge(const jolt::DecodeArgs &a, int nseq, hipStream_t s);
+hipError_t jolt_launch_dense(const jolt::DenseArgs &a, int nseq, hipStream_t s);
+hipError_t jolt_launch_dense_merge(const jolt::DenseArgs &a, int nseq, hipStream_t s);
+hipError_t jolt_launch_unpack(const jolt::LayerDev *layer, int tau, int H, int T, int d,
+                              uint8_t *out, hipStream_t s);
+int jolt_mfma_max_lds();

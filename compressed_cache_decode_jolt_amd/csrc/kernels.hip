@@ -1,0 +1,544 @@
+// Generic split-T decode kernel, split merge/finalize, dense decode kernel and
+// the debug unpack kernel of libjolt (gfx950).
+//
+// What is computed: decode attention over a JoLT-compressed cache ("A JoLT
+// for the KV cache", arXiv 2607.12550v4 summary, Abstract and §4.5: attention
+// directly over the stored factors and packed residuals, keys rebuilt per
+// tile because RoPE does not commute with the factorisation).  The value path
+// uses linearity: each split keeps a = sum_t p_t A_V[t] and c = sum_t p_t
+// deq_V[t]; the merge forms o = (a G_V) B_V^T + c Pi^T.
+//
+// The generic kernel is plain SIMT (fp32 arithmetic, LDS tiles of 32
+// tokens).  It serves float32 caches and shapes the MFMA kernel does not take.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "jolt_internal.h"
+
+using namespace jolt;
+
+namespace {
+
+constexpr int kTT = 32;  // tokens per generic tile
+constexpr int kMergeChunk = 2048;
+
+__device__ inline float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+template <bool F32>
+__device__ inline float ldf(const void *p, size_t i) {
+  if constexpr (F32)
+    return ((const float *)p)[i];
+  else
+    return bf16f(((const uint16_t *)p)[i]);
+}
+
+__device__ inline float ldq(const void *q, size_t i, bool f32) {
+  return f32 ? ((const float *)q)[i] : bf16f(((const uint16_t *)q)[i]);
+}
+
+__device__ inline int k_code(const CellDev &c, int h, int t, int i, int T_pad, int d) {
+  const int b = c.bits;
+  const uint8_t *row = c.codes + ((size_t)h * T_pad + t) * (d * b / 8);
+  int s = i >> 5, g = (i >> 3) & 3, j = i & 7, dw, sh;
+  code_pos(8 * s + j, b, &dw, &sh);
+  uint32_t w = *(const uint32_t *)(row + g * (d * b / 32) + 4 * dw);
+  return (w >> sh) & ((1u << b) - 1u);
+}
+
+__device__ inline int v_code(const CellDev &c, int h, int t, int i, int T_pad, int d) {
+  const int b = c.bits;
+  const uint8_t *p = c.codes + (((size_t)h * (T_pad / 32) + t / 32) * d + i) * (4 * b);
+  int dw, sh;
+  code_pos(perm32_inv(t & 31), b, &dw, &sh);
+  uint32_t w = *(const uint32_t *)(p + 4 * dw);
+  return (w >> sh) & ((1u << b) - 1u);
+}
+
+__device__ inline float deq(int code, int bits, float scale) {
+  return ((float)code - 0.5f * (float)((1 << bits) - 1)) * scale;
+}
+
+// RoPE angle of pair i at position t: the float32 product fl32(t * inv_freq[i]).
+__device__ inline void rope_cs(int t, float f, float *c, float *s) {
+  float a = __fmul_rn((float)t, f);
+  sincosf(a, s, c);
+}
+
+// ------------------------------------------------------------ generic --
+template <bool F32>
+__global__ __launch_bounds__(256) void decode_generic(DecodeArgs a) {
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const SeqArg sa = a.seq[b];
+  const LayerDev &L = *sa.layer;
+  const CellDev &K = L.c[0], &V = L.c[1];
+  const int T = sa.T, T_pad = L.T_pad, d = a.d, Hg = a.Hg, half = d / 2;
+  const int t0 = split * a.split_tokens, t1 = min(T, t0 + a.split_tokens);
+
+  __shared__ float qr[kMaxHg][kMaxD];
+  __shared__ float P[kTT][kMaxD];
+  __shared__ float X[kTT][kMaxD];
+  __shared__ float Kt[kTT][kMaxD];
+  __shared__ float S[kMaxHg][kTT];
+  __shared__ float cacc[kMaxHg][kMaxD];
+  __shared__ float m_s[kMaxHg], l_s[kMaxHg], al_s[kMaxHg];
+
+  float *part0 = a.ws + ((size_t)(b * a.H_q + h * Hg) * a.n_split + split) * a.stride;
+  const size_t ustride = (size_t)a.n_split * a.stride;
+
+  if (t0 >= t1) {  // empty split (shorter sequence in the batch)
+    for (int u = tid; u < Hg; u += 256) {
+      part0[u * ustride + 0] = -INFINITY;
+      part0[u * ustride + 1] = 0.0f;
+    }
+    return;
+  }
+
+  // query heads of this KV head, rotated to q_pos
+  for (int x = tid; x < Hg * half; x += 256) {
+    int u = x / half, i = x % half;
+    size_t qi = ((size_t)b * a.H_q + h * Hg + u) * d;
+    float lo = ldq(a.q, qi + i, a.q_f32), hi = ldq(a.q, qi + i + half, a.q_f32);
+    float c, s;
+    rope_cs(sa.q_pos, a.inv_freq[i], &c, &s);
+    qr[u][i] = lo * c - hi * s;
+    qr[u][i + half] = hi * c + lo * s;
+  }
+  for (int x = tid; x < Hg * d; x += 256) cacc[x / d][x % d] = 0.0f;
+  for (int u = tid; u < Hg; u += 256) {
+    m_s[u] = -INFINITY;
+    l_s[u] = 0.0f;
+  }
+  for (int x = tid; x < Hg * V.rT_pad; x += 256)
+    part0[(x / V.rT_pad) * ustride + 4 + (x % V.rT_pad)] = 0.0f;
+  __syncthreads();
+
+  const float Lk = 0.5f * (float)((1 << K.bits) - 1);
+  for (int tt = t0; tt < t1; tt += kTT) {
+    const int nt = min(kTT, t1 - tt);
+    // P = A_K[t] G_K  (t < nt, j < r_F)
+    for (int x = tid; x < nt * K.rF; x += 256) {
+      int t = x / K.rF, j = x % K.rF;
+      float acc = 0.0f;
+      for (int r = 0; r < K.rT; ++r)
+        acc += ldf<F32>(K.A, (size_t)(tt + t) * K.rT_pad + r) *
+               ldf<F32>(K.G, ((size_t)h * K.rF_pad + j) * K.rT_pad + r);
+      P[t][j] = acc;
+    }
+    // key residual in the rotated basis
+    if (K.bits)
+      for (int x = tid; x < nt * d; x += 256) {
+        int t = x / d, i = x % d;
+        X[t][i] = ((float)k_code(K, h, tt + t, i, T_pad, d) - Lk) *
+                  K.scales[(size_t)h * T_pad + tt + t];
+      }
+    __syncthreads();
+    // K_pre = P B_K^T + deq Pi^T
+    for (int x = tid; x < nt * d; x += 256) {
+      int t = x / d, f = x % d;
+      float acc = 0.0f;
+      for (int j = 0; j < K.rF; ++j) acc += P[t][j] * ldf<F32>(K.B, (size_t)f * K.rF_pad + j);
+      if (K.bits)
+        for (int i = 0; i < d; ++i) acc += X[t][i] * L.Pi[(size_t)f * d + i];
+      Kt[t][f] = acc;
+    }
+    __syncthreads();
+    // RoPE at each token's own position
+    for (int x = tid; x < nt * half; x += 256) {
+      int t = x / half, i = x % half;
+      float c, s;
+      rope_cs(tt + t, a.inv_freq[i], &c, &s);
+      float lo = Kt[t][i], hi = Kt[t][i + half];
+      Kt[t][i] = lo * c - hi * s;
+      Kt[t][i + half] = hi * c + lo * s;
+    }
+    __syncthreads();
+    for (int x = tid; x < Hg * nt; x += 256) {
+      int u = x / nt, t = x % nt;
+      float acc = 0.0f;
+      for (int f = 0; f < d; ++f) acc += qr[u][f] * Kt[t][f];
+      S[u][t] = a.scale * acc;
+    }
+    // value residual (rotated basis) into X
+    const float Lv = 0.5f * (float)((1 << V.bits) - 1);
+    __syncthreads();
+    if (V.bits)
+      for (int x = tid; x < nt * d; x += 256) {
+        int t = x / d, i = x % d;
+        X[t][i] = ((float)v_code(V, h, tt + t, i, T_pad, d) - Lv) *
+                  V.scales[(size_t)h * T_pad + tt + t];
+      }
+    // online softmax
+    if (tid < Hg) {
+      int u = tid;
+      float mt = -INFINITY;
+      for (int t = 0; t < nt; ++t) mt = fmaxf(mt, S[u][t]);
+      float mn = fmaxf(m_s[u], mt);
+      float al = expf(m_s[u] - mn);
+      float sum = 0.0f;
+      for (int t = 0; t < nt; ++t) {
+        float p = expf(S[u][t] - mn);
+        S[u][t] = p;
+        sum += p;
+      }
+      l_s[u] = al * l_s[u] + sum;
+      m_s[u] = mn;
+      al_s[u] = al;
+    }
+    __syncthreads();
+    if (V.bits)
+      for (int x = tid; x < Hg * d; x += 256) {
+        int u = x / d, i = x % d;
+        float acc = 0.0f;
+        for (int t = 0; t < nt; ++t) acc += S[u][t] * X[t][i];
+        cacc[u][i] = al_s[u] * cacc[u][i] + acc;
+      }
+    for (int x = tid; x < Hg * V.rT; x += 256) {
+      int u = x / V.rT, r = x % V.rT;
+      float acc = 0.0f;
+      for (int t = 0; t < nt; ++t) {
+        int tg = tt + t;
+        acc += S[u][t] * ldf<F32>(V.A, (size_t)r * T_pad + (tg & ~31) + perm32_inv(tg & 31));
+      }
+      float *pa = part0 + u * ustride + 4 + r;
+      *pa = al_s[u] * *pa + acc;
+    }
+    __syncthreads();
+  }
+  for (int x = tid; x < Hg * d; x += 256) {
+    int u = x / d, i = x % d;
+    part0[u * ustride + 4 + a.rV_max + i] = cacc[u][i];
+  }
+  for (int u = tid; u < Hg; u += 256) {
+    part0[u * ustride + 0] = m_s[u];
+    part0[u * ustride + 1] = l_s[u];
+  }
+}
+
+// -------------------------------------------------------------- merge --
+// One workgroup per (sequence, KV head): combine the splits of each query
+// head, then o = (a G_V[h]) B_V^T + c Pi^T.
+template <bool F32>
+__global__ __launch_bounds__(256) void merge_finalize(DecodeArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const SeqArg sa = a.seq[b];
+  const LayerDev &L = *sa.layer;
+  const CellDev &V = L.c[1];
+  const int d = a.d, Hg = a.Hg, ns = a.n_split;
+  __shared__ float w_s[kMaxSplits];
+  __shared__ float av[kMergeChunk];
+  __shared__ float cv[kMaxD];
+  __shared__ float yv[kMaxD];
+  __shared__ float red[256];
+  __shared__ float scal[2];
+  for (int u = 0; u < Hg; ++u) {
+    const float *pbase = a.ws + ((size_t)(b * a.H_q + h * Hg + u) * ns) * a.stride;
+    float mx = -INFINITY;
+    for (int s = tid; s < ns; s += 256) mx = fmaxf(mx, pbase[(size_t)s * a.stride]);
+    red[tid] = mx;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+      __syncthreads();
+    }
+    mx = red[0];
+    __syncthreads();
+    float lsum = 0.0f;
+    for (int s = tid; s < ns; s += 256) {
+      float m = pbase[(size_t)s * a.stride];
+      float w = (m == -INFINITY) ? 0.0f : expf(m - mx);
+      w_s[s] = w;
+      lsum += w * pbase[(size_t)s * a.stride + 1];
+    }
+    red[tid] = lsum;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if (tid < o) red[tid] += red[tid + o];
+      __syncthreads();
+    }
+    if (tid == 0) scal[0] = 1.0f / red[0];
+    __syncthreads();
+    const float inv = scal[0];
+    // c (rotated residual space), then y = a G_V[h] chunk by chunk over the
+    // rank so that any r_T fits the LDS staging buffer.
+    const int na = V.rT;
+    for (int i = tid; i < d; i += 256) {
+      float acc = 0.0f;
+      for (int s = 0; s < ns; ++s) {
+        float w = w_s[s];
+        if (w != 0.0f) acc += w * pbase[(size_t)s * a.stride + 4 + a.rV_max + i];
+      }
+      cv[i] = acc * inv;
+    }
+    for (int j = tid; j < kMaxD; j += 256) yv[j] = 0.0f;
+    for (int r0 = 0; r0 < na; r0 += kMergeChunk) {
+      const int nr = min(kMergeChunk, na - r0);
+      __syncthreads();
+      for (int x = tid; x < nr; x += 256) {
+        float acc = 0.0f;
+        for (int s = 0; s < ns; ++s) {
+          float w = w_s[s];
+          if (w != 0.0f) acc += w * pbase[(size_t)s * a.stride + 4 + r0 + x];
+        }
+        av[x] = acc * inv;
+      }
+      __syncthreads();
+      for (int j = tid; j < V.rF; j += 256) {
+        float acc = 0.0f;
+        for (int r = 0; r < nr; ++r)
+          acc += av[r] * ldf<F32>(V.G, ((size_t)h * V.rT_pad + r0 + r) * V.rF_pad + j);
+        yv[j] += acc;
+      }
+    }
+    __syncthreads();
+    for (int f = tid; f < d; f += 256) {
+      float acc = 0.0f;
+      for (int j = 0; j < V.rF; ++j) acc += yv[j] * ldf<F32>(V.B, (size_t)f * V.rF_pad + j);
+      if (V.bits)
+        for (int i = 0; i < d; ++i) acc += cv[i] * L.Pi[(size_t)f * d + i];
+      a.out[((size_t)b * a.H_q + h * Hg + u) * d + f] = acc;
+    }
+    __syncthreads();
+  }
+}
+
+// -------------------------------------------------------------- dense --
+// Flash-decoding over post-RoPE bf16/fp32 K and V.  A group of D/8 lanes owns
+// one token at a time (8 features per lane, one 16-byte load); each group
+// walks U consecutive tokens per step and keeps its own online-softmax state,
+// merged across groups at the end of the split.
+template <int D, int HG, bool KV32>
+__global__ __launch_bounds__(256) void dense_split(DenseArgs a) {
+  constexpr int LPT = D / 8, TPP = 256 / LPT, U = 4;
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int tg = tid / LPT, li = tid % LPT;
+  const int Hg = a.Hg, T = a.T;
+  const int t0 = split * a.split_tokens, t1 = min(T, t0 + a.split_tokens);
+  const int qpos = a.q_pos[b];
+  float qv[HG][8];
+#pragma unroll
+  for (int u = 0; u < HG; ++u) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[u][e] = 0.0f;
+    if (u < Hg) {
+      size_t qi = ((size_t)b * a.H_q + h * Hg + u) * D;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        int f = 8 * li + e, i = f % (D / 2);
+        float c, s;
+        rope_cs(qpos, a.inv_freq[i], &c, &s);
+        float x = ldq(a.q, qi + f, a.q_f32);
+        float y = ldq(a.q, qi + (f < D / 2 ? f + D / 2 : f - D / 2), a.q_f32);
+        qv[u][e] = (f < D / 2 ? x * c - y * s : x * c + y * s) * a.scale;
+      }
+    }
+  }
+  float m[HG], l[HG], acc[HG][8];
+#pragma unroll
+  for (int u = 0; u < HG; ++u) {
+    m[u] = -INFINITY;
+    l[u] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[u][e] = 0.0f;
+  }
+  const size_t base = ((size_t)b * a.H + h) * T * D;
+  for (int tb = t0 + tg * U; tb < t1; tb += TPP * U) {
+    float kf[U][8], vf[U][8];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      int t = tb + k;
+      if (t < t1) {
+        size_t off = base + (size_t)t * D + 8 * li;
+        if constexpr (KV32) {
+          const float4 *kp = (const float4 *)((const float *)a.k + off);
+          const float4 *vp = (const float4 *)((const float *)a.v + off);
+          float4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
+          kf[k][0] = k0.x; kf[k][1] = k0.y; kf[k][2] = k0.z; kf[k][3] = k0.w;
+          kf[k][4] = k1.x; kf[k][5] = k1.y; kf[k][6] = k1.z; kf[k][7] = k1.w;
+          vf[k][0] = v0.x; vf[k][1] = v0.y; vf[k][2] = v0.z; vf[k][3] = v0.w;
+          vf[k][4] = v1.x; vf[k][5] = v1.y; vf[k][6] = v1.z; vf[k][7] = v1.w;
+        } else {
+          uint4 kk = *(const uint4 *)((const uint16_t *)a.k + off);
+          uint4 vv = *(const uint4 *)((const uint16_t *)a.v + off);
+          uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w}, vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kf[k][2 * e] = __uint_as_float(kw[e] << 16);
+            kf[k][2 * e + 1] = __uint_as_float(kw[e] & 0xffff0000u);
+            vf[k][2 * e] = __uint_as_float(vw[e] << 16);
+            vf[k][2 * e + 1] = __uint_as_float(vw[e] & 0xffff0000u);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kf[k][e] = vf[k][e] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < HG; ++u) {
+      if (u >= Hg) break;
+      float s[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        float x = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x += qv[u][e] * kf[k][e];
+#pragma unroll
+        for (int o = LPT / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
+        s[k] = (tb + k < t1) ? x : -INFINITY;
+      }
+      float mt = s[0];
+#pragma unroll
+      for (int k = 1; k < U; ++k) mt = fmaxf(mt, s[k]);
+      float mn = fmaxf(m[u], mt);
+      float al = expf(m[u] - mn);
+      float p[U], ps = 0.0f;
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        p[k] = expf(s[k] - mn);
+        ps += p[k];
+      }
+      l[u] = al * l[u] + ps;
+      m[u] = mn;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = al * acc[u][e];
+#pragma unroll
+        for (int k = 0; k < U; ++k) x += p[k] * vf[k][e];
+        acc[u][e] = x;
+      }
+    }
+  }
+  // merge the lane groups of a wave (lanes 16 apart for D=128, 8 apart for D=64)
+#pragma unroll
+  for (int o = LPT; o < 64; o <<= 1) {
+#pragma unroll
+    for (int u = 0; u < HG; ++u) {
+      float mo = __shfl_xor(m[u], o), lo = __shfl_xor(l[u], o);
+      float mn = fmaxf(m[u], mo);
+      float wa = (m[u] == -INFINITY) ? 0.0f : expf(m[u] - mn);
+      float wb = (mo == -INFINITY) ? 0.0f : expf(mo - mn);
+      l[u] = wa * l[u] + wb * lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[u][e] = wa * acc[u][e] + wb * __shfl_xor(acc[u][e], o);
+      m[u] = mn;
+    }
+  }
+  __shared__ float sm[4][HG], sl[4][HG], sacc[4][HG][D];
+  const int wave = tid / 64, lane = tid % 64;
+  if (lane < LPT) {
+#pragma unroll
+    for (int u = 0; u < HG; ++u) {
+      if (lane == 0) {
+        sm[wave][u] = m[u];
+        sl[wave][u] = l[u];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sacc[wave][u][8 * lane + e] = acc[u][e];
+    }
+  }
+  __syncthreads();
+  for (int x = tid; x < Hg * D; x += 256) {
+    int u = x / D, f = x % D;
+    float mx = fmaxf(fmaxf(sm[0][u], sm[1][u]), fmaxf(sm[2][u], sm[3][u]));
+    float ls = 0.0f, as = 0.0f;
+    for (int w = 0; w < 4; ++w) {
+      float wt = sm[w][u] == -INFINITY ? 0.0f : expf(sm[w][u] - mx);
+      ls += wt * sl[w][u];
+      as += wt * sacc[w][u][f];
+    }
+    float *part = a.ws + ((size_t)(b * a.H_q + h * Hg + u) * a.n_split + split) * (4 + D);
+    if (f == 0) {
+      part[0] = mx;
+      part[1] = ls;
+    }
+    part[4 + f] = as;
+  }
+}
+
+__global__ __launch_bounds__(128) void dense_merge(DenseArgs a) {
+  const int j = blockIdx.x, b = blockIdx.y, f = threadIdx.x, D = a.d;
+  const float *pb = a.ws + ((size_t)(b * a.H_q + j) * a.n_split) * (4 + D);
+  float mx = -INFINITY;
+  for (int s = 0; s < a.n_split; ++s) mx = fmaxf(mx, pb[(size_t)s * (4 + D)]);
+  float ls = 0.0f, as = 0.0f;
+  for (int s = 0; s < a.n_split; ++s) {
+    float m = pb[(size_t)s * (4 + D)];
+    float w = m == -INFINITY ? 0.0f : expf(m - mx);
+    ls += w * pb[(size_t)s * (4 + D) + 1];
+    if (f < D) as += w * pb[(size_t)s * (4 + D) + 4 + f];
+  }
+  if (f < D) a.out[((size_t)b * a.H_q + j) * D + f] = as / ls;
+}
+
+// ------------------------------------------------------------- unpack --
+__global__ void unpack_codes(const LayerDev *layer, int tau, int H, int T, int d, uint8_t *out) {
+  const LayerDev &L = *layer;
+  const CellDev &c = L.c[tau];
+  size_t n = (size_t)H * T * d;
+  for (size_t x = blockIdx.x * (size_t)blockDim.x + threadIdx.x; x < n;
+       x += (size_t)gridDim.x * blockDim.x) {
+    int i = x % d;
+    int t = (x / d) % T;
+    int h = x / ((size_t)d * T);
+    out[x] = (uint8_t)(tau == 0 ? k_code(c, h, t, i, L.T_pad, d) : v_code(c, h, t, i, L.T_pad, d));
+  }
+}
+
+}  // namespace
+
+hipError_t jolt_launch_generic(const DecodeArgs &a, int nseq, hipStream_t s) {
+  dim3 grid(a.n_split, a.H, nseq);
+  if (a.f32)
+    hipLaunchKernelGGL(decode_generic<true>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_generic<false>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t jolt_launch_merge(const DecodeArgs &a, int nseq, hipStream_t s) {
+  dim3 grid(a.H, nseq);
+  if (a.f32)
+    hipLaunchKernelGGL(merge_finalize<true>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(merge_finalize<false>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D, bool KV32>
+static void launch_dense_hg(const DenseArgs &a, dim3 grid, hipStream_t s) {
+  if (a.Hg <= 1)
+    hipLaunchKernelGGL((dense_split<D, 1, KV32>), grid, dim3(256), 0, s, a);
+  else if (a.Hg <= 2)
+    hipLaunchKernelGGL((dense_split<D, 2, KV32>), grid, dim3(256), 0, s, a);
+  else if (a.Hg <= 4)
+    hipLaunchKernelGGL((dense_split<D, 4, KV32>), grid, dim3(256), 0, s, a);
+  else if (a.Hg <= 8)
+    hipLaunchKernelGGL((dense_split<D, 8, KV32>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((dense_split<D, 16, KV32>), grid, dim3(256), 0, s, a);
+}
+
+hipError_t jolt_launch_dense(const DenseArgs &a, int nseq, hipStream_t s) {
+  dim3 grid(a.n_split, a.H, nseq);
+  if (a.d == 128)
+    a.kv_f32 ? launch_dense_hg<128, true>(a, grid, s) : launch_dense_hg<128, false>(a, grid, s);
+  else
+    a.kv_f32 ? launch_dense_hg<64, true>(a, grid, s) : launch_dense_hg<64, false>(a, grid, s);
+  return hipGetLastError();
+}
+
+hipError_t jolt_launch_dense_merge(const DenseArgs &a, int nseq, hipStream_t s) {
+  hipLaunchKernelGGL(dense_merge, dim3(a.H_q, nseq), dim3(128), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t jolt_launch_unpack(const LayerDev *layer, int tau, int H, int T, int d, uint8_t *out,
+                              hipStream_t s) {
+  size_t n = (size_t)H * T * d;
+  int blocks = (int)((n + 255) / 256);
+  if (blocks > 65535) blocks = 65535;
+  hipLaunchKernelGGL(unpack_codes, dim3(blocks), dim3(256), 0, s, layer, tau, H, T, d, out);
+  return hipGetLastError();
+}

@@ -1,0 +1,241 @@
+"""GPU parity: the HIP decode path (through the C ABI) against the oracle.
+
+Every case feeds the same seeded compressed cache to both sides and compares
+element by element:
+  * float32 caches (the tiny workload): rel-L2 <= 1e-5;
+  * bf16 caches, generic kernel (fp32 arithmetic): rel-L2 <= 1e-5;
+  * bf16 caches, MFMA kernel: rel-L2 <= 5e-3 and max-abs <= 2e-2;
+  * residual codes read back from the device layout: bit-exact.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import compressed_cache_decode_jolt_amd as J
+from oracle import attention as att
+from oracle.compress import compress
+from oracle.quant import unpack
+from oracle.rope import rope
+from oracle.rotation import rotation
+from workloads import gen, get_config
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    J.lib()
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def run_decode(caches, layer, q, q_pos, inv, scale, q_dtype="bf16", kernel=None, split=0,
+               handles=None):
+    hs = handles or [J.jolt_load_cache(c) for c in caches]
+    dt = torch.bfloat16 if q_dtype == "bf16" else torch.float32
+    qt = torch.from_numpy(np.asarray(q, dtype=np.float32)).to(dt).cuda()
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    nb = J.jolt_decode_workspace_size(hs, layer, kernel=kernel, split_tokens=split)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    J.jolt_decode_attention(hs, layer, qt, q_pos, inv, scale, out, ws, kernel=kernel,
+                            split_tokens=split)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def oracle_decode(caches, layer, q, q_pos, inv, scale):
+    return att.decode_attention(caches, layer, np.asarray(q, np.float64), q_pos, inv, scale)
+
+
+KERNELS = [J.KERNEL_GENERIC]
+
+
+def tol(kernel, f32):
+    if kernel == J.KERNEL_MFMA:
+        return 5e-3, 2e-2
+    return 1e-5, 1e-4
+
+
+# ------------------------------------------------------------ bit-exact --
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("T", [1, 37, 300])
+def test_unpack_bit_exact(bits, T):
+    c = gen.small_cache(bits, T, 3, 6, 128, [((16, 16, bits), (32, 16, bits))], [2])
+    h = J.jolt_load_cache(c)
+    for layer in range(2):
+        for tau in range(2):
+            got = J.jolt_debug_unpack(h, layer, tau)
+            want = unpack(c["cells"][0][tau]["codes"][layer], bits, 128)
+            assert np.array_equal(got, want)
+
+
+def test_unpack_d64_oracle_codes():
+    cfg = get_config(0)
+    groups = [(gen.kv_group(cfg, 0, 0, 0), gen.kv_group(cfg, 0, 0, 1))]
+    c = compress(groups, [((32, 16, 4), (32, 16, 2))], "f32", 7, cfg.H_q, [0, 1])
+    h = J.jolt_load_cache(c)
+    for tau, b in ((0, 4), (1, 2)):
+        assert np.array_equal(J.jolt_debug_unpack(h, 0, tau),
+                              unpack(c["cells"][0][tau]["codes"][0], b, 64))
+
+
+# ------------------------------------------------------------- workloads --
+def tiny_cache():
+    cfg = get_config(0)
+    groups = [(gen.kv_group(cfg, 0, 0, 0), gen.kv_group(cfg, 0, 0, 1))]
+    return cfg, compress(groups, [(cfg.fixed, cfg.fixed)], "f32", 0x4A4F4C54, cfg.H_q,
+                         cfg.group_start())
+
+
+def test_tiny_fp32_workload():
+    cfg, c = tiny_cache()
+    inv = gen.rope_inv_freq_input(cfg.rope_base, cfg.d)
+    q = gen.cfg_queries(cfg, 0, 0)[None]
+    scale = 1 / math.sqrt(cfg.d)
+    got = run_decode([c], 0, q, [cfg.T], inv, scale, "f32")
+    want = oracle_decode([c], 0, q, [cfg.T], inv, scale)
+    assert rel_l2(got, want) <= 1e-5, rel_l2(got, want)
+
+
+def layer8b_cache():
+    cfg = get_config(1)
+    import json, os
+    alloc = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "allocations.json")))
+    (aK, aV), = alloc["1"]["tables"]["3x"]["groups"]
+    groups = [(gen.kv_group(cfg, 0, 0, 0), gen.kv_group(cfg, 0, 0, 1))]
+    return cfg, compress(groups, [(tuple(aK), tuple(aV))], "bf16", 0x4A4F4C54, cfg.H_q,
+                         cfg.group_start())
+
+
+@pytest.fixture(scope="module")
+def l8b():
+    return layer8b_cache()
+
+
+@pytest.mark.parametrize("kernel", [None] + KERNELS)
+def test_llama8b_layer_workload(l8b, kernel):
+    cfg, c = l8b
+    inv = gen.rope_inv_freq_input(cfg.rope_base, cfg.d)
+    q = gen.cfg_queries(cfg, 0, 0)[None]
+    scale = 1 / math.sqrt(cfg.d)
+    got = run_decode([c], 0, q, [cfg.T], inv, scale, kernel=kernel)
+    want = oracle_decode([c], 0, q, [cfg.T], inv, scale)
+    r, mx = rel_l2(got, want), float(np.max(np.abs(got - want)))
+    print(f"llama8b layer kernel={kernel}: rel_l2={r:.3e} max_abs={mx:.3e}")
+    assert r <= 5e-3 and mx <= 2e-2
+
+
+# ------------------------------------------------------------- coverage --
+BITS = [0, 2, 4, 8]
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("bK", BITS)
+@pytest.mark.parametrize("bV", BITS)
+def test_bits_matrix_ragged(bK, bV, kernel):
+    T, H, H_q, d = 300, 2, 8, 128
+    c = gen.small_cache(10 * bK + bV, T, H, H_q, d, [((40, 24, bK), (33, 17, bV))], [1])
+    inv = gen.rope_inv_freq_input(5e5, d)
+    q = gen.queries(77, bK, bV, H_q, d, "bf16")[None]
+    got = run_decode([c], 0, q, [T], inv, 0.09, kernel=kernel)
+    want = oracle_decode([c], 0, q, [T], inv, 0.09)
+    r, a = tol(kernel, False)
+    assert rel_l2(got, want) <= r and np.max(np.abs(got - want)) <= a
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_split_invariance(kernel):
+    T = 1000
+    c = gen.small_cache(5, T, 4, 16, 128, [((64, 32, 4), (96, 64, 2))], [1])
+    inv = gen.rope_inv_freq_input(1e4, 128)
+    q = gen.queries(78, 0, 0, 16, 128, "bf16")[None]
+    hs = [J.jolt_load_cache(c)]
+    outs = [run_decode([c], 0, q, [T], inv, 0.1, kernel=kernel, split=s, handles=hs)
+            for s in (0, 128, 256, 1024)]
+    for o in outs[1:]:
+        assert rel_l2(o, outs[0]) <= 2e-6
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_batch_of_different_lengths_and_ranks(kernel):
+    d, H, H_q = 128, 2, 4
+    caches = [gen.small_cache(20 + i, T, H, H_q, d, [(aK, aV)], [1])
+              for i, (T, aK, aV) in enumerate([(100, (16, 16, 2), (16, 16, 8)),
+                                                (257, (48, 32, 4), (64, 32, 4)),
+                                                (1000, (32, 64, 0), (128, 96, 2))])]
+    inv = gen.rope_inv_freq_input(5e5, d)
+    q = np.stack([gen.queries(79, i, 0, H_q, d, "bf16") for i in range(3)])
+    q_pos = [100, 300, 1000]
+    got = run_decode(caches, 0, q, q_pos, inv, 0.088, kernel=kernel)
+    want = oracle_decode(caches, 0, q, q_pos, inv, 0.088)
+    r, a = tol(kernel, False)
+    for b in range(3):
+        assert rel_l2(got[b], want[b]) <= r
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_layer_groups(kernel):
+    d, H, H_q, T = 128, 2, 8, 200
+    c = gen.small_cache(30, T, H, H_q, d, [((32, 16, 4), (64, 32, 2)), ((16, 16, 8), (16, 32, 0))],
+                        [3, 2])
+    inv = gen.rope_inv_freq_input(5e5, d)
+    hs = [J.jolt_load_cache(c)]
+    for layer in range(5):
+        q = gen.queries(80, 0, layer, H_q, d, "bf16")[None]
+        got = run_decode([c], layer, q, [T], inv, 0.1, kernel=kernel, handles=hs)
+        want = oracle_decode([c], layer, q, [T], inv, 0.1)
+        assert rel_l2(got, want) <= tol(kernel, False)[0], layer
+
+
+def test_degenerate_cases():
+    d, H, H_q = 128, 1, 4
+    inv = gen.rope_inv_freq_input(1e4, d)
+    # T = 1: the output is V^_0 for every query head
+    c = gen.small_cache(40, 1, H, H_q, d, [((16, 16, 4), (16, 16, 4))], [1])
+    q = gen.queries(81, 0, 0, H_q, d, "bf16")[None]
+    got = run_decode([c], 0, q, [0], inv, 0.1)
+    assert rel_l2(got, oracle_decode([c], 0, q, [0], inv, 0.1)) <= 1e-5
+    # no value factors and no value residual: the output is exactly 0
+    c = gen.small_cache(41, 50, H, H_q, d, [((16, 16, 4), (0, 0, 0))], [1])
+    got = run_decode([c], 0, q, [50], inv, 0.1)
+    assert np.all(got == 0)
+    # residual only (no Tucker part)
+    c = gen.small_cache(42, 70, H, H_q, d, [((0, 0, 8), (0, 0, 2))], [1])
+    got = run_decode([c], 0, q, [70], inv, 0.1)
+    assert rel_l2(got, oracle_decode([c], 0, q, [70], inv, 0.1)) <= 1e-5
+    # q = 0: uniform attention, the mean of V^
+    c = gen.small_cache(43, 77, H, H_q, d, [((16, 16, 4), (32, 16, 4))], [1])
+    got = run_decode([c], 0, np.zeros((1, H_q, d)), [77], inv, 0.1)
+    Vh = att.decode_cell(c["cells"][0][1], 0, d, rotation(c["rotation_seed"], d))
+    assert rel_l2(got[0], np.repeat(Vh.mean(axis=1), H_q // H, axis=0)) <= 1e-5
+
+
+# ------------------------------------------------------------------ dense --
+@pytest.mark.parametrize("d,H,H_q,T", [(128, 8, 32, 4096), (128, 2, 16, 333), (64, 2, 8, 256),
+                                       (128, 4, 4, 1000)])
+@pytest.mark.parametrize("kv", ["bf16", "f32"])
+def test_dense_parity(d, H, H_q, T, kv):
+    g = np.random.default_rng(T + d)
+    inv = gen.rope_inv_freq_input(5e5, d)
+    K = rope(g.standard_normal((2, H, T, d)) * 1.3, np.arange(T), inv)
+    V = g.standard_normal((2, H, T, d)) * 3.0
+    if kv == "bf16":
+        K, V = gen.to_bf16_values(K).astype(np.float64), gen.to_bf16_values(V).astype(np.float64)
+    q = np.stack([gen.queries(82, b, 0, H_q, d, "bf16") for b in range(2)]).astype(np.float64)
+    dt = torch.bfloat16 if kv == "bf16" else torch.float32
+    kt = torch.from_numpy(K.astype(np.float32)).to(dt).cuda()
+    vt = torch.from_numpy(V.astype(np.float32)).to(dt).cuda()
+    qt = torch.from_numpy(q.astype(np.float32)).to(torch.bfloat16).cuda()
+    out = torch.empty((2, H_q, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(J.jolt_dense_workspace_size(2, H, H_q, d, T), dtype=torch.uint8, device="cuda")
+    J.jolt_dense_attention(kt, vt, qt, [T, T + 5], inv, 1 / math.sqrt(d), out, ws)
+    torch.cuda.synchronize()
+    want = att.dense_attention(K, V, q, [T, T + 5], inv, 1 / math.sqrt(d))
+    assert rel_l2(out.cpu().numpy(), want) <= 1e-5

@@ -158,3 +158,25 @@ def rope_inv_freq_input(base, d):
     """
     i = np.arange(d // 2, dtype=np.float64)
     return (float(base) ** (-2.0 * i / d)).astype(np.float32)
+
+
+def small_cache(seed, T, H, H_q, d, alloc, group_sizes, factor_dtype="bf16",
+                sigma=(1.3, 3.4), rotation_seed=ROTATION_SEED):
+    """A synthetic compressed cache of arbitrary shape for parity tests.
+
+    ``alloc[g] = ((r_T, r_F, b) K, (r_T, r_F, b) V)``; ``group_sizes[g]`` =
+    layers in group g.
+    """
+    cells = []
+    for grp, gs in enumerate(group_sizes):
+        pair = []
+        for tau in (0, 1):
+            r_T, r_F, b = alloc[grp][tau]
+            g = rng(1000 + seed, 0, grp, tau, P_SYN)
+            pair.append(synthetic_cell(g, T, d, gs, H, r_T, r_F, b, factor_dtype, sigma[tau]))
+        cells.append(pair)
+    starts = [0]
+    for gs in group_sizes:
+        starts.append(starts[-1] + gs)
+    return {"T": T, "H": H, "H_q": H_q, "d": d, "n_layers": starts[-1], "group_start": starts,
+            "factor_dtype": factor_dtype, "rotation_seed": rotation_seed, "cells": cells}
