@@ -1,0 +1,279 @@
+"""Decode-attention benchmark over JoLT-compressed KV caches on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--ratio 3x]
+
+A step is one decode step of the workload: every layer of every sequence
+(one jolt_decode_attention call per layer, all sequences batched) with the
+compressed caches already resident in HBM.  The default workload is one
+Llama-3.1-8B-shaped layer (8 KV / 32 query heads, d=128, T=4096, batch 1)
+compressed at the allocator's 3x budget.  Small caches are rotated over enough
+device copies (> 512 MiB) that a step reads HBM, not the 256 MiB Infinity
+Cache.  Prints one JSON line: compressed-context tokens/s, the dominant
+kernel's roofline position (timed live with HIP events around that kernel),
+the dense decode comparator on the same shape and the CPU oracle baseline.
+"""
+import argparse
+import ctypes as C
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
+PEAK_MFMA_BF16 = 2.5e15    # FLOP/s, dense bf16/fp16 MFMA
+MALL_BYTES = 256 << 20
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on its stream)."""
+
+    def __init__(self):
+        self.hip = C.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = C.c_void_p()
+            assert self.hip.hipEventCreate(C.byref(e)) == 0
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        f = C.c_float()
+        assert self.hip.hipEventSynchronize(C.c_void_p(b)) == 0
+        assert self.hip.hipEventElapsedTime(C.byref(f), C.c_void_p(a), C.c_void_p(b)) == 0
+        return f.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(C.c_void_p(e))
+
+
+def load_alloc(cfg, ratio):
+    path = os.path.join(ROOT, "tests", "golden", "allocations.json")
+    tables = json.load(open(path))[str(cfg.idx)]["tables"]
+    key = ratio if ratio in tables else ("fixed" if "fixed" in tables else sorted(tables)[0])
+    return key, [tuple(map(tuple, g)) for g in tables[key]["groups"]]
+
+
+def algorithmic(cfg, alloc, layer):
+    """Bytes and MFMA FLOPs of one layer call for one sequence (unpadded ranks)."""
+    g = layer // cfg.group_size
+    (rTk, rFk, bk), (rTv, rFv, bv) = alloc[g]
+    T, H, Hq, d, sf = cfg.T, cfg.H, cfg.H_q, cfg.d, cfg.factor_bytes
+    sq = 4 if cfg.q_dtype == "f32" else 2
+    nbytes = (T * sf * (rTk + rTv) + H * T * (d * (bk + bv) // 8 + 4 * ((bk > 0) + (bv > 0)))
+              + sf * (H * (rTk * rFk + rTv * rFv) + d * (rFk + rFv)) + sf * d * d
+              + Hq * d * (sq + 4))
+    flops = (T * H * (2 * rTk * rFk + 2 * (rFk + d * (bk > 0)) * d) + T * Hq * 2 * d
+             + T * Hq * 2 * (rTv + d * (bv > 0)))
+    return nbytes, flops
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "compressed_cache_decode_jolt_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel_name):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, only if
+    the kernel sources are unchanged since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(f"{workload}/{kernel_name}")
+    if not rec or rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec["bytes_per_launch"]
+
+
+def cpu_baseline(cfg, cache, seconds):
+    """The oracle decode (numpy float64) on the host cores, bounded sample."""
+    from oracle import attention as att
+    from oracle.rotation import rotation
+    from workloads import gen
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    inv = gen.rope_inv_freq_input(cfg.rope_base, cfg.d)
+    Pi = rotation(cache["rotation_seed"], cfg.d)
+    q = gen.cfg_queries(cfg, 0, 0).astype(np.float64)
+    calls, t0 = 0, time.perf_counter()
+    layer = 0
+    while True:
+        att.decode_layer(cache, layer, q, cfg.T, inv, 1 / math.sqrt(cfg.d), Pi)
+        calls += 1
+        layer = (layer + 1) % cache["n_layers"]
+        el = time.perf_counter() - t0
+        if el >= seconds or (calls >= 3 and el * (calls + 1) / calls > 3 * seconds):
+            break
+    per_call = el / calls
+    step = per_call * cfg.n_layers * cfg.batch
+    return {"value": cfg.batch * cfg.T / step, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{calls} single-sequence layer calls of this workload's cache "
+                      f"({el:.1f} s), scaled to a full step of {cfg.n_layers} layers x "
+                      f"{cfg.batch} sequences"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--ratio", default="3x")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "mfma"])
+    ap.add_argument("--split-tokens", type=int, default=0, help="tokens per split (0 = auto)")
+    ap.add_argument("--dense-split-tokens", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build measures the single-GPU decode path "
+              "(the multi-GPU sharding is described, not run)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import compressed_cache_decode_jolt_amd as J
+    from workloads import gen, get_config
+
+    cfg = get_config(args.config)
+    ratio_key, alloc = load_alloc(cfg, args.ratio)
+    kernel = {"auto": None, "generic": J.KERNEL_GENERIC, "mfma": J.KERNEL_MFMA}[args.kernel]
+    B, L, H, Hq, d, T = cfg.batch, cfg.n_layers, cfg.H, cfg.H_q, cfg.d, cfg.T
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # caches: one synthetic cache per sequence, loaded `copies` times
+    host = [gen.synthetic_cache(cfg, alloc, seq=s) for s in range(B)]
+    step_bytes = B * sum(algorithmic(cfg, alloc, l)[0] for l in range(L))
+    copies = max(1, math.ceil(2 * MALL_BYTES / step_bytes))
+    caches = [[J.jolt_load_cache(host[s]) for s in range(B)] for _ in range(copies)]
+    inv = gen.rope_inv_freq_input(cfg.rope_base, d)
+    scale = 1.0 / math.sqrt(d)
+    qdt = torch.bfloat16 if cfg.q_dtype == "bf16" else torch.float32
+    qs = [torch.from_numpy(np.stack([gen.cfg_queries(cfg, s, l) for s in range(B)])).to(qdt).to(dev)
+          for l in range(L)]
+    q_pos = [T] * B
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    split = args.split_tokens
+    ws_bytes = max(J.jolt_decode_workspace_size(caches[0], l, kernel=kernel, split_tokens=split)
+                   for l in range(L))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ev = HipEvents()
+    n_ev = args.steps * L
+    evb, eve = ev.create(n_ev), ev.create(n_ev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, timed):
+        cs = caches[i % copies]
+        for l in range(L):
+            e = (evb[(i * L + l) % n_ev], eve[(i * L + l) % n_ev]) if timed else None
+            J.jolt_decode_attention(cs, l, qs[l], q_pos, inv, scale, out, ws, kernel=kernel,
+                                    split_tokens=split, stream=stream, events=e)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    for i in range(args.steps):
+        step(i, True)
+    t_stop.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_stop) / args.steps
+    split_ms = [ev.elapsed_ms(a, b) for a, b in zip(evb, eve)]
+    ev.destroy(evb + eve)
+    kern_ms = float(np.mean(split_ms))
+
+    per_launch = [algorithmic(cfg, alloc, l) for l in range(L)]
+    bytes_launch = B * float(np.mean([p[0] for p in per_launch]))
+    flops_launch = B * float(np.mean([p[1] for p in per_launch]))
+    mfma_bound = flops_launch / PEAK_MFMA_BF16 > bytes_launch / PEAK_HBM
+    kname = "decode_split"
+    if mfma_bound:
+        achieved = flops_launch / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_BF16 / 1e12,
+                "unit": "TFLOP/s", "frac": achieved / (PEAK_MFMA_BF16 / 1e12)}
+    else:
+        achieved = bytes_launch / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                "frac": achieved / (PEAK_HBM / 1e9)}
+    roof["traffic"] = measured_traffic(cfg.name, kname)
+    roof["kernel_ms"] = kern_ms
+    roof["alg_bytes_per_launch"] = bytes_launch
+    roof["alg_flops_per_launch"] = flops_launch
+
+    # dense comparator on the same shape (random bf16 post-RoPE K and V)
+    dense = None
+    if not args.no_dense:
+        dense_step = 2 * B * L * H * T * d * 2
+        dcopies = max(1, math.ceil(2 * MALL_BYTES / dense_step))
+        g = torch.Generator(device=dev).manual_seed(0)
+        kv = [[(torch.randn((B, H, T, d), generator=g, device=dev).to(torch.bfloat16),
+                torch.randn((B, H, T, d), generator=g, device=dev).to(torch.bfloat16))
+               for _ in range(L)] for _ in range(dcopies)]
+        dsplit = args.dense_split_tokens
+        dws = torch.empty(J.jolt_dense_workspace_size(B, H, Hq, d, T, split_tokens=dsplit),
+                          dtype=torch.uint8, device=dev)
+
+        def dstep(i):
+            for l in range(L):
+                k, v = kv[i % dcopies][l]
+                J.jolt_dense_attention(k, v, qs[l], q_pos, inv, scale, out, dws,
+                                       split_tokens=dsplit, stream=stream)
+
+        for i in range(args.warmup):
+            dstep(i)
+        torch.cuda.synchronize()
+        t_start.record()
+        for i in range(args.steps):
+            dstep(i)
+        t_stop.record()
+        torch.cuda.synchronize()
+        dms = t_start.elapsed_time(t_stop) / args.steps
+        dense = {"ms_per_step": dms, "hbm_GBps": dense_step / (dms * 1e-3) / 1e9,
+                 "jolt_speedup": dms / ms_per_step}
+        del kv
+
+    cpu = None if args.no_cpu else cpu_baseline(cfg, host[0], args.cpu_seconds)
+    value = B * T / (ms_per_step * 1e-3)
+    rec = {
+        "metric": "compressed-context tokens/s per decode step",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": B, "layers": L, "kv_heads": H, "q_heads": Hq,
+                   "head_dim": d, "T": T, "budget": ratio_key,
+                   "allocation": [list(map(list, a)) for a in alloc[:1]] if L == 1 else ratio_key,
+                   "kernel": args.kernel, "split_tokens": split, "cache_copies": copies,
+                   "step_alg_bytes": step_bytes},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "dense": dense,
+        "step_hbm_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+    }
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

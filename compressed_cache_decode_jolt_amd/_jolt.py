@@ -38,7 +38,8 @@ class jolt_cache_desc(C.Structure):
 
 
 class jolt_launch(C.Structure):
-    _fields_ = [("kernel", C.c_int32), ("split_tokens", C.c_int32)]
+    _fields_ = [("kernel", C.c_int32), ("split_tokens", C.c_int32),
+                ("ev_begin", C.c_void_p), ("ev_end", C.c_void_p)]
 
 
 _lib = None
@@ -62,6 +63,7 @@ EXPORTS = {
     "jolt_last_error": (C.c_char_p, []),
     "jolt_make_rotation": (C.c_int, [C.c_uint64, C.c_int32, C.POINTER(C.c_double)]),
     "jolt_debug_unpack": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
+    "jolt_debug_sincos": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p]),
 }
 
 
@@ -98,10 +100,11 @@ def _stream(stream):
     return C.c_void_p(stream.cuda_stream)
 
 
-def _launch(kernel=None, split_tokens=0):
-    if kernel is None and not split_tokens:
+def _launch(kernel=None, split_tokens=0, events=None):
+    if kernel is None and not split_tokens and events is None:
         return None
-    return jolt_launch(int(kernel or 0), int(split_tokens))
+    ev = events or (None, None)
+    return jolt_launch(int(kernel or 0), int(split_tokens), ev[0], ev[1])
 
 
 def _factor_bytes(x, dtype):
@@ -209,13 +212,15 @@ def _dtype_code(t):
 
 
 def jolt_decode_attention(caches, layer, q, q_pos, inv_freq, softmax_scale, out, workspace,
-                          kernel=None, split_tokens=0, stream=None):
+                          kernel=None, split_tokens=0, stream=None, events=None):
     """q: device tensor [B, H_q, d] (f32/bf16); out: device f32 [B, H_q, d];
-    workspace: device tensor of at least jolt_decode_workspace_size bytes."""
+    workspace: device tensor of at least jolt_decode_workspace_size bytes;
+    events: optional (begin, end) raw hipEvent_t handles recorded around the
+    split-T kernel."""
     B = len(caches)
     qp = (C.c_int32 * max(1, B))(*[int(x) for x in q_pos])
     inv = np.ascontiguousarray(inv_freq, dtype=np.float32)
-    L = _launch(kernel, split_tokens)
+    L = _launch(kernel, split_tokens, events)
     _check(lib().jolt_decode_attention(
         _handles(caches), B, layer, _ptr(q), _dtype_code(q), qp,
         inv.ctypes.data_as(C.POINTER(C.c_float)), C.c_float(softmax_scale), _ptr(out),
@@ -255,3 +260,10 @@ def jolt_debug_unpack(cache, layer, tau, stream=None):
     out = np.empty((m["H"], m["T"], m["d"]), dtype=np.uint8)
     _check(lib().jolt_debug_unpack(cache.handle, layer, tau, out.ctypes.data, _stream(stream)))
     return out
+
+
+def jolt_debug_sincos(angles):
+    x = np.ascontiguousarray(angles, dtype=np.float32)
+    sn, cs = np.empty_like(x), np.empty_like(x)
+    _check(lib().jolt_debug_sincos(x.ctypes.data, x.size, sn.ctypes.data, cs.ctypes.data))
+    return sn, cs

@@ -184,9 +184,13 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
   try {
     size_t off_pi = S.take(sizeof(float) * d * d);
     for (int i = 0; i < d * d; ++i) ((float *)(S.buf.data() + off_pi))[i] = (float)Pi64[i];
+    size_t off_pit = S.take(sizeof(float) * d * d);
+    for (int r = 0; r < d; ++r)
+      for (int c2 = 0; c2 < d; ++c2)
+        ((float *)(S.buf.data() + off_pit))[(size_t)c2 * d + r] = (float)Pi64[(size_t)r * d + c2];
 
     struct Offs {
-      size_t A, B, W;
+      size_t A, B, Bt, W;
       std::vector<size_t> G, codes, scales;  // per layer in group
     };
     std::vector<Offs> offs(2 * c->n_groups);
@@ -218,6 +222,12 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
           for (int j = 0; j < m.rF; ++j)
             store_factor(S.buf.data() + o.B, (size_t)f * m.rF_pad + j, in.B, (size_t)f * m.rF + j,
                          f32);
+        // B^T in float32 for the value finalize
+        o.Bt = S.take(sizeof(float) * std::max(m.rF_pad, 1) * d);
+        for (int f = 0; f < d; ++f)
+          for (int j = 0; j < m.rF; ++j)
+            ((float *)(S.buf.data() + o.Bt))[(size_t)j * d + f] =
+                load_factor(in.B, (size_t)f * m.rF + j, f32);
         // W = [B_K (slot-permuted) | Pi] in fp16, keys of bf16 caches only
         o.W = 0;
         if (tau == 0 && !f32) {
@@ -296,6 +306,7 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
       LayerDev &L = c->h_layers[l];
       std::memset(&L, 0, sizeof L);
       L.Pi = (const float *)(base + off_pi);
+      L.PiT = (const float *)(base + off_pit);
       L.T = T;
       L.T_pad = T_pad;
       L.f32 = f32 ? 1 : 0;
@@ -305,6 +316,7 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
         CellDev &cd = L.c[tau];
         cd.A = base + o.A;
         cd.B = base + o.B;
+        cd.Bt = (const float *)(base + o.Bt);
         cd.G = base + o.G[lp];
         cd.W = o.W ? (const _Float16 *)(base + o.W) : nullptr;
         cd.codes = m.bits ? base + o.codes[lp] : nullptr;
@@ -361,15 +373,20 @@ struct Plan {
   int kernel;        // JOLT_KERNEL_GENERIC or JOLT_KERNEL_MFMA
   int split_tokens, n_split, rV_max, stride, T_max;
   int lds_bytes;     // MFMA only
+  int nkt;           // MFMA only: max key-rank steps of 32
   size_t ws_bytes;
 };
 
+// The MFMA kernel stages G_K[h]^T and W = [B_K | Pi] in LDS (rows padded by
+// 8 elements) next to 8.5 KiB of exchange buffers and 8 KiB of rotated
+// queries, prefetches up to 256 key ranks a tile ahead in registers and keeps
+// the value-rank accumulators of up to 512 ranks in registers.
 static bool mfma_ok(const jolt_cache *c, int layer, int *lds) {
   if (c->f32 || c->d != 128) return false;
   const LayerDev &L = c->h_layers[layer];
   const CellDev &k = L.c[0], &v = L.c[1];
-  if (v.rT_pad > 1024 || k.rT_pad > 1024) return false;
-  int bytes = 2 * k.rF_pad * k.rT_pad + 2 * c->d * k.kw + 32768;
+  if (v.rT_pad > 512 || k.rT_pad > 256) return false;
+  int bytes = 2 * k.rF_pad * (k.rT_pad + 8) + 2 * c->d * (k.kw + 8) + 8704 + 16 * 128 * 4;
   *lds = bytes;
   return bytes <= jolt_mfma_max_lds();
 }
@@ -397,17 +414,24 @@ static jolt_status plan_decode(const jolt_cache *const *caches, int batch, int l
   p->rV_max = 0;
   bool mf = batch > 0;
   p->lds_bytes = 0;
+  p->nkt = 0;
   for (int b = 0; b < batch; ++b) {
     const jolt_cache *c = caches[b];
     p->T_max = std::max(p->T_max, c->T);
     p->rV_max = std::max(p->rV_max, c->h_layers[layer].c[1].rT_pad);
     int lds = 0;
     if (!mfma_ok(c, layer, &lds)) mf = false;
+    // one launch runs one (key bits, value bits) instantiation
+    if (c->h_layers[layer].c[0].bits != c0->h_layers[layer].c[0].bits ||
+        c->h_layers[layer].c[1].bits != c0->h_layers[layer].c[1].bits)
+      mf = false;
     p->lds_bytes = std::max(p->lds_bytes, lds);
+    p->nkt = std::max(p->nkt, c->h_layers[layer].c[0].rT_pad / 32);
   }
   if (want == JOLT_KERNEL_MFMA && !mf)
     return fail(JOLT_E_UNSUPPORTED,
-                "MFMA kernel needs bf16 factors, d=128, ranks <= 1024 and an LDS fit");
+                "MFMA kernel needs bf16 factors, d=128, key rank <= 256, value rank <= 512, an LDS fit for "
+                "G_K and [B_K|Pi], and the same key/value bits for every sequence");
   p->kernel = (want == JOLT_KERNEL_GENERIC || !mf) ? JOLT_KERNEL_GENERIC : JOLT_KERNEL_MFMA;
   const int tile = p->kernel == JOLT_KERNEL_MFMA ? kTokPad : 32;
   int H = batch ? c0->H : 1;
@@ -482,11 +506,19 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
       a.seq[i].q_pos = q_pos[b0 + i];
       a.seq[i].T = caches[b0 + i]->T;
     }
-    hipError_t e = p.kernel == JOLT_KERNEL_MFMA
+    hipError_t e = hipSuccess;
+    if (launch && launch->ev_begin && b0 == 0)
+      e = hipEventRecord((hipEvent_t)launch->ev_begin, s);
+    if (e != hipSuccess) return fail(JOLT_E_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+    e = p.kernel == JOLT_KERNEL_MFMA
                        ? jolt_launch_mfma(a, nb, caches[b0]->h_layers[layer].c[0].bits,
-                                          caches[b0]->h_layers[layer].c[1].bits, p.lds_bytes, s)
+                                          caches[b0]->h_layers[layer].c[1].bits, p.nkt,
+                                          p.lds_bytes, s)
                        : jolt_launch_generic(a, nb, s);
     if (e != hipSuccess) return fail(JOLT_E_HIP, "split kernel launch: %s", hipGetErrorString(e));
+    if (launch && launch->ev_end && b0 + nb >= batch)
+      e = hipEventRecord((hipEvent_t)launch->ev_end, s);
+    if (e != hipSuccess) return fail(JOLT_E_HIP, "hipEventRecord: %s", hipGetErrorString(e));
     e = jolt_launch_merge(a, nb, s);
     if (e != hipSuccess) return fail(JOLT_E_HIP, "merge kernel launch: %s", hipGetErrorString(e));
   }
@@ -507,6 +539,7 @@ static jolt_status plan_dense(int batch, int n_kv, int n_q, int d, int T, const 
     split = (T + n - 1) / n;
   }
   *split_tokens = round_up(std::max(split, 1), 64);
+  *split_tokens = std::max(*split_tokens, round_up((T + kMaxSplits - 1) / kMaxSplits, 64));
   *n_split = (T + *split_tokens - 1) / *split_tokens;
   *bytes = (size_t)batch * n_q * *n_split * (4 + d) * sizeof(float);
   return JOLT_OK;
@@ -598,5 +631,21 @@ extern "C" jolt_status jolt_debug_unpack(const jolt_cache *c, int32_t layer, int
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   hipFree(dbuf);
   if (e != hipSuccess) return fail(JOLT_E_HIP, "debug unpack: %s", hipGetErrorString(e));
+  return ok();
+}
+
+extern "C" jolt_status jolt_debug_sincos(const float *angles, int32_t n, float *sin_out,
+                                         float *cos_out) {
+  if (n < 0 || (n > 0 && (!angles || !sin_out || !cos_out)))
+    return fail(JOLT_E_INVALID, "NULL argument or n < 0");
+  if (n == 0) return ok();
+  float *d = nullptr;
+  HIP_TRY(hipMalloc(&d, sizeof(float) * 3 * (size_t)n));
+  hipError_t e = hipMemcpy(d, angles, sizeof(float) * n, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = jolt_launch_sincos(d, n, d + n, d + 2 * (size_t)n, nullptr);
+  if (e == hipSuccess) e = hipMemcpy(sin_out, d + n, sizeof(float) * n, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(cos_out, d + 2 * (size_t)n, sizeof(float) * n, hipMemcpyDeviceToHost);
+  hipFree(d);
+  if (e != hipSuccess) return fail(JOLT_E_HIP, "debug sincos: %s", hipGetErrorString(e));
   return ok();
 }

@@ -54,6 +54,7 @@ struct CellDev {
   // [H][rT_pad][rF_pad].
   const void *G;
   const void *B;          // [d][rF_pad], factor dtype
+  const float *Bt;        // V: B^T as float32, [rF_pad][d] (finalize reads)
   const _Float16 *W;      // K, bf16 caches: [d][kw] fp16 = [B_K | Pi] (see host)
   // Residual codes of this layer.
   // K: [H][T_pad][d*b/8]; a row is 4 chunks (one per 16-lane group g) of
@@ -69,6 +70,7 @@ struct CellDev {
 struct LayerDev {
   CellDev c[2];           // [0] = K, [1] = V
   const float *Pi;        // [d][d] float32, row-major
+  const float *PiT;       // Pi^T, [d][d] float32 (finalize reads)
   int32_t T, T_pad, f32;  // f32: factors stored as float32 (else bf16)
 };
 
@@ -116,13 +118,39 @@ struct DenseArgs {
 
 }  // namespace jolt
 
+// Copy rows of 16-byte chunks from global memory to LDS with every thread
+// keeping up to 8 loads in flight (a plain load-then-store loop would pay
+// one memory round trip per chunk).  src rows are src_cpr chunks long and
+// contiguous; dst rows start every dst_stride bytes.
+__device__ inline void stage_rows(uint8_t *dst, int dst_stride, const uint8_t *src, int rows,
+                                  int src_cpr, int tid, int nthreads) {
+  const int n = rows * src_cpr;
+  for (int x0 = 0; x0 < n; x0 += 8 * nthreads) {
+    uint4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int x = x0 + k * nthreads + tid;
+      if (x < n) v[k] = ((const uint4 *)src)[x];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int x = x0 + k * nthreads + tid;
+      if (x < n) {
+        const int r = x / src_cpr, c = x - r * src_cpr;
+        *(uint4 *)(dst + (size_t)r * dst_stride + 16 * c) = v[k];
+      }
+    }
+  }
+}
+
 // Kernel launchers (kernels_*.hip).  Each returns the hipError_t of its launch.
 hipError_t jolt_launch_generic(const jolt::DecodeArgs &a, int nseq, hipStream_t s);
-hipError_t jolt_launch_mfma(const jolt::DecodeArgs &a, int nseq, int bK, int bV, int lds_bytes,
-                            hipStream_t s);
+hipError_t jolt_launch_mfma(const jolt::DecodeArgs &a, int nseq, int bK, int bV, int nkt,
+                            int lds_bytes, hipStream_t s);
 hipError_t jolt_launch_merge(const jolt::DecodeArgs &a, int nseq, hipStream_t s);
 hipError_t jolt_launch_dense(const jolt::DenseArgs &a, int nseq, hipStream_t s);
 hipError_t jolt_launch_dense_merge(const jolt::DenseArgs &a, int nseq, hipStream_t s);
 hipError_t jolt_launch_unpack(const jolt::LayerDev *layer, int tau, int H, int T, int d,
                               uint8_t *out, hipStream_t s);
+hipError_t jolt_launch_sincos(const float *x, int n, float *sn, float *cs, hipStream_t s);
 int jolt_mfma_max_lds();

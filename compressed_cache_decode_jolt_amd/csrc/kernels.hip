@@ -16,6 +16,7 @@
 #include <stdint.h>
 
 #include "jolt_internal.h"
+#include "trig.h"
 
 using namespace jolt;
 
@@ -61,10 +62,7 @@ __device__ inline float deq(int code, int bits, float scale) {
 }
 
 // RoPE angle of pair i at position t: the float32 product fl32(t * inv_freq[i]).
-__device__ inline void rope_cs(int t, float f, float *c, float *s) {
-  float a = __fmul_rn((float)t, f);
-  sincosf(a, s, c);
-}
+__device__ inline void rope_cs(int t, float f, float *c, float *s) { rope_angle_cs(t, f, c, s); }
 
 // ------------------------------------------------------------ generic --
 template <bool F32>
@@ -217,90 +215,123 @@ __global__ __launch_bounds__(256) void decode_generic(DecodeArgs a) {
 }
 
 // -------------------------------------------------------------- merge --
-// One workgroup per (sequence, KV head): combine the splits of each query
-// head, then o = (a G_V[h]) B_V^T + c Pi^T.
+// One workgroup per (sequence, query head j): combine the split partials
+// (weights w_s = exp(m_s - max m), a = sum w_s a_s / sum w_s l_s, c alike),
+// then finalize o = (a G_V[h]) B_V^T + c Pi^T with h = j / Hg.
+__device__ inline float block_reduce(float v, float *red, bool is_max) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float w = __shfl_xor(v, o);
+    v = is_max ? fmaxf(v, w) : v + w;
+  }
+  if ((tid & 63) == 0) red[tid >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
+  __syncthreads();
+  return r;
+}
+
+// Weighted sum over splits of partial column `off` for columns
+// col0 + tid, col0 + tid + nthreads, ...: loads are issued in batches of 16
+// splits so that many are in flight per thread.
+__device__ inline void split_columns(const float *pb, int st, int ns, const float *w_s,
+                                     int ncol, int off0, float inv, float *dst, int tid,
+                                     int nthreads) {
+  for (int x = tid; x < ncol; x += nthreads) {
+    float acc = 0.0f;
+    for (int s0 = 0; s0 < ns; s0 += 16) {
+      float v[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = s0 + k < ns ? pb[(size_t)(s0 + k) * st + off0 + x] : 0.0f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (s0 + k < ns) acc += w_s[s0 + k] * v[k];
+    }
+    dst[x] = acc * inv;
+  }
+}
+
 template <bool F32>
 __global__ __launch_bounds__(256) void merge_finalize(DecodeArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int j = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int Hg = a.Hg, h = j / Hg, d = a.d, ns = a.n_split;
   const SeqArg sa = a.seq[b];
   const LayerDev &L = *sa.layer;
   const CellDev &V = L.c[1];
-  const int d = a.d, Hg = a.Hg, ns = a.n_split;
   __shared__ float w_s[kMaxSplits];
   __shared__ float av[kMergeChunk];
   __shared__ float cv[kMaxD];
-  __shared__ float yv[kMaxD];
-  __shared__ float red[256];
-  __shared__ float scal[2];
-  for (int u = 0; u < Hg; ++u) {
-    const float *pbase = a.ws + ((size_t)(b * a.H_q + h * Hg + u) * ns) * a.stride;
-    float mx = -INFINITY;
-    for (int s = tid; s < ns; s += 256) mx = fmaxf(mx, pbase[(size_t)s * a.stride]);
-    red[tid] = mx;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-      if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-      __syncthreads();
-    }
-    mx = red[0];
-    __syncthreads();
-    float lsum = 0.0f;
-    for (int s = tid; s < ns; s += 256) {
-      float m = pbase[(size_t)s * a.stride];
-      float w = (m == -INFINITY) ? 0.0f : expf(m - mx);
-      w_s[s] = w;
-      lsum += w * pbase[(size_t)s * a.stride + 1];
-    }
-    red[tid] = lsum;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-      if (tid < o) red[tid] += red[tid + o];
-      __syncthreads();
-    }
-    if (tid == 0) scal[0] = 1.0f / red[0];
-    __syncthreads();
-    const float inv = scal[0];
-    // c (rotated residual space), then y = a G_V[h] chunk by chunk over the
-    // rank so that any r_T fits the LDS staging buffer.
-    const int na = V.rT;
-    for (int i = tid; i < d; i += 256) {
-      float acc = 0.0f;
-      for (int s = 0; s < ns; ++s) {
-        float w = w_s[s];
-        if (w != 0.0f) acc += w * pbase[(size_t)s * a.stride + 4 + a.rV_max + i];
-      }
-      cv[i] = acc * inv;
-    }
-    for (int j = tid; j < kMaxD; j += 256) yv[j] = 0.0f;
-    for (int r0 = 0; r0 < na; r0 += kMergeChunk) {
-      const int nr = min(kMergeChunk, na - r0);
-      __syncthreads();
-      for (int x = tid; x < nr; x += 256) {
-        float acc = 0.0f;
-        for (int s = 0; s < ns; ++s) {
-          float w = w_s[s];
-          if (w != 0.0f) acc += w * pbase[(size_t)s * a.stride + 4 + r0 + x];
-        }
-        av[x] = acc * inv;
-      }
-      __syncthreads();
-      for (int j = tid; j < V.rF; j += 256) {
-        float acc = 0.0f;
-        for (int r = 0; r < nr; ++r)
-          acc += av[r] * ldf<F32>(V.G, ((size_t)h * V.rT_pad + r0 + r) * V.rF_pad + j);
-        yv[j] += acc;
-      }
-    }
-    __syncthreads();
-    for (int f = tid; f < d; f += 256) {
-      float acc = 0.0f;
-      for (int j = 0; j < V.rF; ++j) acc += yv[j] * ldf<F32>(V.B, (size_t)f * V.rF_pad + j);
-      if (V.bits)
-        for (int i = 0; i < d; ++i) acc += cv[i] * L.Pi[(size_t)f * d + i];
-      a.out[((size_t)b * a.H_q + h * Hg + u) * d + f] = acc;
-    }
-    __syncthreads();
+  __shared__ float yv[2][kMaxD];
+  __shared__ float ov[2][kMaxD];
+  __shared__ float red[8];
+  __shared__ __attribute__((aligned(16))) float mat[kMaxD * kMaxD];  // staged Pi^T or B_V^T
+  const float *pb = a.ws + ((size_t)(b * a.H_q + j) * ns) * a.stride;
+  const int st = a.stride;
+
+  float mx = -INFINITY;
+  for (int s = tid; s < ns; s += 256) {
+    float m = pb[(size_t)s * st];
+    w_s[s] = m;
+    mx = fmaxf(mx, m);
   }
+  mx = block_reduce(mx, red, true);
+  float ls = 0.0f;
+  for (int s = tid; s < ns; s += 256) {
+    float m = w_s[s];
+    float w = (m == -INFINITY) ? 0.0f : __expf(m - mx);
+    w_s[s] = w;
+    ls += w * pb[(size_t)s * st + 1];
+  }
+  ls = block_reduce(ls, red, false);  // also orders the w_s writes
+  const float inv = 1.0f / ls;
+
+  split_columns(pb, st, ns, w_s, d, 4 + a.rV_max, inv, cv, tid, 256);
+  // y = a G_V[h]: two thread halves split the rank sum, chunk by chunk
+  const int na = V.rT, half = tid >> 7, jj = tid & 127;
+  float yacc = 0.0f;
+  for (int r0 = 0; r0 < na; r0 += kMergeChunk) {
+    const int nr = min(kMergeChunk, na - r0);
+    __syncthreads();
+    split_columns(pb, st, ns, w_s, nr, 4 + r0, inv, av, tid, 256);
+    __syncthreads();
+    if (jj < V.rF) {
+      float g[8];
+      for (int r = half; r < nr; r += 16) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          g[k] = r + 2 * k < nr ? ldf<F32>(V.G, ((size_t)h * V.rT_pad + r0 + r + 2 * k) * V.rF_pad + jj)
+                                : 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (r + 2 * k < nr) yacc += av[r + 2 * k] * g[k];
+      }
+    }
+  }
+  yv[half][jj] = yacc;
+  __syncthreads();
+  if (tid < 128) yv[0][tid] += yv[1][tid];
+  // o = y B_V^T + c Pi^T with each matrix staged in LDS by bulk loads
+  float acc = 0.0f;
+  const int f = tid & 127, part = tid >> 7;
+  if (V.rF > 0) {
+    __syncthreads();
+    stage_rows((uint8_t *)mat, 4 * d, (const uint8_t *)V.Bt, V.rF, d / 4, tid, 256);
+    __syncthreads();
+    if (f < d)
+      for (int q = part; q < V.rF; q += 2) acc += yv[0][q] * mat[q * d + f];
+  }
+  if (V.bits) {
+    __syncthreads();
+    stage_rows((uint8_t *)mat, 4 * d, (const uint8_t *)L.PiT, d, d / 4, tid, 256);
+    __syncthreads();
+    if (f < d)
+      for (int i = part; i < d; i += 2) acc += cv[i] * mat[i * d + f];
+  }
+  if (f < d) ov[part][f] = acc;
+  __syncthreads();
+  if (tid < d) a.out[((size_t)b * a.H_q + j) * d + tid] = ov[0][tid] + ov[1][tid];
 }
 
 // -------------------------------------------------------------- dense --
@@ -316,24 +347,23 @@ __global__ __launch_bounds__(256) void dense_split(DenseArgs a) {
   const int Hg = a.Hg, T = a.T;
   const int t0 = split * a.split_tokens, t1 = min(T, t0 + a.split_tokens);
   const int qpos = a.q_pos[b];
+  // the workgroup's query heads rotated to q_pos (one pair per thread), scaled
+  __shared__ float qs[HG][D];
+  for (int x = tid; x < Hg * (D / 2); x += 256) {
+    const int u = x / (D / 2), i = x % (D / 2);
+    const size_t qi = ((size_t)b * a.H_q + h * Hg + u) * D;
+    float c, s;
+    rope_cs(qpos, a.inv_freq[i], &c, &s);
+    const float lo = ldq(a.q, qi + i, a.q_f32), hi = ldq(a.q, qi + i + D / 2, a.q_f32);
+    qs[u][i] = (lo * c - hi * s) * a.scale;
+    qs[u][i + D / 2] = (hi * c + lo * s) * a.scale;
+  }
+  __syncthreads();
   float qv[HG][8];
 #pragma unroll
-  for (int u = 0; u < HG; ++u) {
+  for (int u = 0; u < HG; ++u)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qv[u][e] = 0.0f;
-    if (u < Hg) {
-      size_t qi = ((size_t)b * a.H_q + h * Hg + u) * D;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        int f = 8 * li + e, i = f % (D / 2);
-        float c, s;
-        rope_cs(qpos, a.inv_freq[i], &c, &s);
-        float x = ldq(a.q, qi + f, a.q_f32);
-        float y = ldq(a.q, qi + (f < D / 2 ? f + D / 2 : f - D / 2), a.q_f32);
-        qv[u][e] = (f < D / 2 ? x * c - y * s : x * c + y * s) * a.scale;
-      }
-    }
-  }
+    for (int e = 0; e < 8; ++e) qv[u][e] = u < Hg ? qs[u][8 * li + e] : 0.0f;
   float m[HG], l[HG], acc[HG][8];
 #pragma unroll
   for (int u = 0; u < HG; ++u) {
@@ -458,18 +488,30 @@ __global__ __launch_bounds__(256) void dense_split(DenseArgs a) {
 }
 
 __global__ __launch_bounds__(128) void dense_merge(DenseArgs a) {
-  const int j = blockIdx.x, b = blockIdx.y, f = threadIdx.x, D = a.d;
-  const float *pb = a.ws + ((size_t)(b * a.H_q + j) * a.n_split) * (4 + D);
+  const int j = blockIdx.x, b = blockIdx.y, f = threadIdx.x, D = a.d, ns = a.n_split;
+  const int st = 4 + D;
+  const float *pb = a.ws + ((size_t)(b * a.H_q + j) * ns) * st;
+  __shared__ float w_s[kMaxSplits];
+  __shared__ float red[8];
   float mx = -INFINITY;
-  for (int s = 0; s < a.n_split; ++s) mx = fmaxf(mx, pb[(size_t)s * (4 + D)]);
-  float ls = 0.0f, as = 0.0f;
-  for (int s = 0; s < a.n_split; ++s) {
-    float m = pb[(size_t)s * (4 + D)];
-    float w = m == -INFINITY ? 0.0f : expf(m - mx);
-    ls += w * pb[(size_t)s * (4 + D) + 1];
-    if (f < D) as += w * pb[(size_t)s * (4 + D) + 4 + f];
+  for (int s = f; s < ns; s += 128) {
+    float m = pb[(size_t)s * st];
+    w_s[s] = m;
+    mx = fmaxf(mx, m);
   }
-  if (f < D) a.out[((size_t)b * a.H_q + j) * D + f] = as / ls;
+  mx = block_reduce(mx, red, true);
+  float ls = 0.0f;
+  for (int s = f; s < ns; s += 128) {
+    float m = w_s[s];
+    float w = m == -INFINITY ? 0.0f : __expf(m - mx);
+    w_s[s] = w;
+    ls += w * pb[(size_t)s * st + 1];
+  }
+  ls = block_reduce(ls, red, false);
+  __shared__ float o_s[kMaxD];
+  split_columns(pb, st, ns, w_s, D, 4, 1.0f / ls, o_s, f, 128);
+  __syncthreads();
+  if (f < D) a.out[((size_t)b * a.H_q + j) * D + f] = o_s[f];
 }
 
 // ------------------------------------------------------------- unpack --
@@ -486,7 +528,17 @@ __global__ void unpack_codes(const LayerDev *layer, int tau, int H, int T, int d
   }
 }
 
+__global__ void sincos_kernel(const float *x, int n, float *sn, float *cs) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) fast_sincos(x[i], sn + i, cs + i);
+}
+
 }  // namespace
+
+hipError_t jolt_launch_sincos(const float *x, int n, float *sn, float *cs, hipStream_t s) {
+  hipLaunchKernelGGL(sincos_kernel, dim3((n + 255) / 256), dim3(256), 0, s, x, n, sn, cs);
+  return hipGetLastError();
+}
 
 hipError_t jolt_launch_generic(const DecodeArgs &a, int nseq, hipStream_t s) {
   dim3 grid(a.n_split, a.H, nseq);
@@ -498,7 +550,7 @@ hipError_t jolt_launch_generic(const DecodeArgs &a, int nseq, hipStream_t s) {
 }
 
 hipError_t jolt_launch_merge(const DecodeArgs &a, int nseq, hipStream_t s) {
-  dim3 grid(a.H, nseq);
+  dim3 grid(a.H_q, nseq);
   if (a.f32)
     hipLaunchKernelGGL(merge_finalize<true>, grid, dim3(256), 0, s, a);
   else

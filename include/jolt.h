@@ -94,6 +94,9 @@ typedef struct {
   int32_t kernel;        /* jolt_kernel                                           */
   int32_t split_tokens;  /* tokens per split-T work item (0 = auto); rounded up   */
                          /* to the kernel's tile                                  */
+  void *ev_begin;        /* optional hipEvent_t recorded on the stream right      */
+  void *ev_end;          /* before / after the split-T kernel (NULL = none), so a */
+                         /* caller can time that kernel alone                      */
 } jolt_launch;
 
 /*
@@ -170,7 +173,7 @@ jolt_status jolt_dense_attention(const void *k_rope, const void *v, jolt_dtype k
 const char *jolt_last_error(void);
 
 /*
- * Test helpers.
+ * Test helpers (not on the decode path).
  * jolt_make_rotation: the rotation the library regenerates from `seed`
  *   (SplitMix64 -> Box-Muller Gaussian d x d, row-major -> Householder QR ->
  *   Q with columns scaled by sign(diag R)), written to HOST out[d*d]
@@ -181,6 +184,9 @@ const char *jolt_last_error(void);
  *   JOLT_E_INVALID if that cell has bits == 0.
  */
 jolt_status jolt_make_rotation(uint64_t seed, int32_t d, double *out);
+/* jolt_debug_sincos: the kernels' float32 sine and cosine of HOST angles[n]
+ *   (evaluated on the current device; synchronous), written to HOST outputs. */
+jolt_status jolt_debug_sincos(const float *angles, int32_t n, float *sin_out, float *cos_out);
 jolt_status jolt_debug_unpack(const jolt_cache *cache, int32_t layer, int32_t tau,
                               uint8_t *codes_out, jolt_stream stream);
 
