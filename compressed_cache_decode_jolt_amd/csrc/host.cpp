@@ -21,6 +21,19 @@ void make_rotation(uint64_t seed, int d, double *out);
 
 using namespace jolt;
 
+// RoPE angles t * inv_freq are evaluated by a reduction valid below 2^20 rad
+// (trig.h): positions are limited to 2^20 and frequencies to [0, 1].
+static constexpr int kMaxPos = 1 << 20;
+
+static jolt_status check_rope(const int32_t *q_pos, int batch, const float *inv_freq, int d) {
+  for (int b = 0; b < batch; ++b)
+    if (q_pos[b] < 0 || q_pos[b] > kMaxPos)
+      return JOLT_E_INVALID;
+  for (int i = 0; i < d / 2; ++i)
+    if (!(inv_freq[i] >= 0.0f && inv_freq[i] <= 1.0f)) return JOLT_E_INVALID;
+  return JOLT_OK;
+}
+
 // ---------------------------------------------------------------- errors --
 static thread_local std::string g_err;
 
@@ -91,7 +104,7 @@ static jolt_status validate_desc(const jolt_cache_desc *d) {
     return fail(JOLT_E_UNSUPPORTED, "query heads per KV head %d > %d",
                 d->n_q_heads / d->n_kv_heads, kMaxHg);
   if (d->T < 1) return fail(JOLT_E_INVALID, "T=%d must be >= 1", d->T);
-  if ((int64_t)d->T > (1 << 24)) return fail(JOLT_E_UNSUPPORTED, "T=%d too large", d->T);
+  if (d->T > kMaxPos) return fail(JOLT_E_UNSUPPORTED, "T=%d > %d", d->T, kMaxPos);
   if (d->factor_dtype != JOLT_F32 && d->factor_dtype != JOLT_BF16)
     return fail(JOLT_E_INVALID, "factor_dtype=%d", (int)d->factor_dtype);
   if (!d->group_start || !d->cells) return fail(JOLT_E_INVALID, "group_start or cells is NULL");
@@ -188,10 +201,15 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
     for (int r = 0; r < d; ++r)
       for (int c2 = 0; c2 < d; ++c2)
         ((float *)(S.buf.data() + off_pit))[(size_t)c2 * d + r] = (float)Pi64[(size_t)r * d + c2];
+    size_t off_pih = S.take(sizeof(_Float16) * d * d);
+    for (int r = 0; r < d; ++r)
+      for (int c2 = 0; c2 < d; ++c2)
+        ((_Float16 *)(S.buf.data() + off_pih))[(size_t)r * d + c2] =
+            (_Float16)Pi64[(size_t)r * d + (c2 & ~31) + perm32(c2 & 31)];
 
     struct Offs {
       size_t A, B, Bt, W;
-      std::vector<size_t> G, codes, scales;  // per layer in group
+      std::vector<size_t> G, W2, codes, scales;  // per layer in group
     };
     std::vector<Offs> offs(2 * c->n_groups);
     c->cells.resize(2 * c->n_groups);
@@ -256,6 +274,28 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
                                       : ((size_t)h * m.rT_pad + r) * m.rF_pad + j;
                 store_factor(S.buf.data() + og, dst, in.G, src, f32);
               }
+          // value finalize matrix W2[h] = B_V G_V[lp, h]^T (bf16 caches)
+          if (tau == 1 && !f32 && m.rT > 0) {
+            size_t ow = S.take(sizeof(_Float16) * H * d * m.rT_pad);
+            o.W2.push_back(ow);
+            _Float16 *W2 = (_Float16 *)(S.buf.data() + ow);
+            std::vector<double> Bf((size_t)d * m.rF), Gf((size_t)m.rT * m.rF);
+            for (size_t i = 0; i < Bf.size(); ++i) Bf[i] = load_factor(in.B, i, false);
+            for (int hh = 0; hh < H; ++hh) {
+              for (size_t i = 0; i < Gf.size(); ++i)
+                Gf[i] = load_factor(in.G, ((size_t)lp * H + hh) * m.rT * m.rF + i, false);
+              for (int f = 0; f < d; ++f)
+                for (int col = 0; col < m.rT_pad; ++col) {
+                  int r = (col & ~31) + perm32(col & 31);
+                  double acc = 0.0;
+                  if (r < m.rT)
+                    for (int j = 0; j < m.rF; ++j) acc += Bf[(size_t)f * m.rF + j] * Gf[(size_t)r * m.rF + j];
+                  W2[((size_t)hh * d + f) * m.rT_pad + col] = (_Float16)acc;
+                }
+            }
+          } else {
+            o.W2.push_back(0);
+          }
           if (m.bits == 0) {
             o.codes.push_back(0);
             o.scales.push_back(0);
@@ -307,6 +347,7 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
       std::memset(&L, 0, sizeof L);
       L.Pi = (const float *)(base + off_pi);
       L.PiT = (const float *)(base + off_pit);
+      L.PiH = (const _Float16 *)(base + off_pih);
       L.T = T;
       L.T_pad = T_pad;
       L.f32 = f32 ? 1 : 0;
@@ -319,6 +360,7 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
         cd.Bt = (const float *)(base + o.Bt);
         cd.G = base + o.G[lp];
         cd.W = o.W ? (const _Float16 *)(base + o.W) : nullptr;
+        cd.W2 = o.W2[lp] ? (const _Float16 *)(base + o.W2[lp]) : nullptr;
         cd.codes = m.bits ? base + o.codes[lp] : nullptr;
         cd.scales = m.bits ? (const float *)(base + o.scales[lp]) : nullptr;
         cd.rT = m.rT;
@@ -378,15 +420,16 @@ struct Plan {
 };
 
 // The MFMA kernel stages G_K[h]^T and W = [B_K | Pi] in LDS (rows padded by
-// 8 elements) next to 8.5 KiB of exchange buffers and 8 KiB of rotated
-// queries, prefetches up to 256 key ranks a tile ahead in registers and keeps
+// 8 elements) next to 8.5 KiB of exchange buffers, 8 KiB of rotated
+// queries and the epilogue's exchange of the value partials, prefetches up to 256 key ranks a tile ahead in registers and keeps
 // the value-rank accumulators of up to 512 ranks in registers.
 static bool mfma_ok(const jolt_cache *c, int layer, int *lds) {
   if (c->f32 || c->d != 128) return false;
   const LayerDev &L = c->h_layers[layer];
   const CellDev &k = L.c[0], &v = L.c[1];
   if (v.rT_pad > 512 || k.rT_pad > 256) return false;
-  int bytes = 2 * k.rF_pad * (k.rT_pad + 8) + 2 * c->d * (k.kw + 8) + 8704 + 16 * 128 * 4;
+  int bytes = 2 * k.rF_pad * (k.rT_pad + 8) + 2 * c->d * (k.kw + 8) + 8704 + 16 * 128 * 4 +
+              512 * (v.rT_pad / 16 + 8);
   *lds = bytes;
   return bytes <= jolt_mfma_max_lds();
 }
@@ -444,7 +487,8 @@ static jolt_status plan_decode(const jolt_cache *const *caches, int batch, int l
   p->split_tokens = round_up(std::max(split, 1), tile);
   p->split_tokens = std::max(p->split_tokens, round_up((p->T_max + kMaxSplits - 1) / kMaxSplits, tile));
   p->n_split = (p->T_max + p->split_tokens - 1) / p->split_tokens;
-  p->stride = partial_stride(p->rV_max, batch ? c0->d : 0);
+  p->stride = p->kernel == JOLT_KERNEL_MFMA ? 4 + (batch ? c0->d : 0)
+                                            : partial_stride(p->rV_max, batch ? c0->d : 0);
   p->ws_bytes = (size_t)batch * (batch ? c0->H_q : 0) * p->n_split * p->stride * sizeof(float);
   return JOLT_OK;
 }
@@ -473,8 +517,8 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
   if (!q || !q_pos || !inv_freq || !out) return fail(JOLT_E_INVALID, "NULL q/q_pos/inv_freq/out");
   if (q_dtype != JOLT_F32 && q_dtype != JOLT_BF16) return fail(JOLT_E_INVALID, "q_dtype");
   if (!std::isfinite(softmax_scale)) return fail(JOLT_E_INVALID, "softmax_scale not finite");
-  for (int b = 0; b < batch; ++b)
-    if (q_pos[b] < 0) return fail(JOLT_E_INVALID, "q_pos[%d]=%d < 0", b, q_pos[b]);
+  if (check_rope(q_pos, batch, inv_freq, caches[0]->d) != JOLT_OK)
+    return fail(JOLT_E_INVALID, "q_pos must lie in [0, 2^20] and inv_freq in [0, 1]");
   if (!workspace || ws_bytes < p.ws_bytes)
     return fail(JOLT_E_WORKSPACE, "workspace %zu bytes, need %zu", workspace ? ws_bytes : 0,
                 p.ws_bytes);
@@ -519,7 +563,7 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
     if (launch && launch->ev_end && b0 + nb >= batch)
       e = hipEventRecord((hipEvent_t)launch->ev_end, s);
     if (e != hipSuccess) return fail(JOLT_E_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-    e = jolt_launch_merge(a, nb, s);
+    e = p.kernel == JOLT_KERNEL_MFMA ? jolt_launch_merge_outputs(a, nb, s) : jolt_launch_merge(a, nb, s);
     if (e != hipSuccess) return fail(JOLT_E_HIP, "merge kernel launch: %s", hipGetErrorString(e));
   }
   return ok();
@@ -571,8 +615,9 @@ extern "C" jolt_status jolt_dense_attention(const void *k_rope, const void *v, j
   if ((kv_dtype != JOLT_F32 && kv_dtype != JOLT_BF16) || (q_dtype != JOLT_F32 && q_dtype != JOLT_BF16))
     return fail(JOLT_E_INVALID, "dtype");
   if (!std::isfinite(softmax_scale)) return fail(JOLT_E_INVALID, "softmax_scale not finite");
-  for (int b = 0; b < batch; ++b)
-    if (q_pos[b] < 0) return fail(JOLT_E_INVALID, "q_pos[%d]=%d < 0", b, q_pos[b]);
+  if (check_rope(q_pos, batch, inv_freq, d) != JOLT_OK)
+    return fail(JOLT_E_INVALID, "q_pos must lie in [0, 2^20] and inv_freq in [0, 1]");
+  if (T > kMaxPos) return fail(JOLT_E_UNSUPPORTED, "T=%d > %d", T, kMaxPos);
   if (!workspace || ws_bytes < need)
     return fail(JOLT_E_WORKSPACE, "workspace %zu bytes, need %zu", workspace ? ws_bytes : 0, need);
   DenseArgs a;
@@ -638,6 +683,9 @@ extern "C" jolt_status jolt_debug_sincos(const float *angles, int32_t n, float *
                                          float *cos_out) {
   if (n < 0 || (n > 0 && (!angles || !sin_out || !cos_out)))
     return fail(JOLT_E_INVALID, "NULL argument or n < 0");
+  for (int i = 0; i < n; ++i)
+    if (!(std::fabs(angles[i]) < (float)kMaxPos))
+      return fail(JOLT_E_INVALID, "angle %g outside (-2^20, 2^20)", (double)angles[i]);
   if (n == 0) return ok();
   float *d = nullptr;
   HIP_TRY(hipMalloc(&d, sizeof(float) * 3 * (size_t)n));

@@ -56,6 +56,9 @@ struct CellDev {
   const void *B;          // [d][rF_pad], factor dtype
   const float *Bt;        // V: B^T as float32, [rF_pad][d] (finalize reads)
   const _Float16 *W;      // K, bf16 caches: [d][kw] fp16 = [B_K | Pi] (see host)
+  // V, bf16 caches: W2 = B_V G_V[h]^T of this layer, [H][d][rT_pad] fp16,
+  // columns in perm32 order inside each 32-block (finalize on MFMA)
+  const _Float16 *W2;
   // Residual codes of this layer.
   // K: [H][T_pad][d*b/8]; a row is 4 chunks (one per 16-lane group g) of
   //    d*b/32 bytes; chunk g holds rotated features i = 32s + 8g + j as slot
@@ -71,6 +74,7 @@ struct LayerDev {
   CellDev c[2];           // [0] = K, [1] = V
   const float *Pi;        // [d][d] float32, row-major
   const float *PiT;       // Pi^T, [d][d] float32 (finalize reads)
+  const _Float16 *PiH;    // Pi in fp16, [d][d], columns perm32 inside 32-blocks
   int32_t T, T_pad, f32;  // f32: factors stored as float32 (else bf16)
 };
 
@@ -94,8 +98,10 @@ struct DecodeArgs {
   SeqArg seq[kMaxBatchPerLaunch];
 };
 
-// A partial is [m, l, 0, 0, a[rV_max], c[d]] (floats); m = -inf, l = 0 for
-// an empty split.
+// A generic-kernel partial is [m, l, 0, 0, a[rV_max], c[d]] (floats); an
+// MFMA-kernel or dense partial is [m, l, 0, 0, o[d]] with o already
+// projected to output space and divided by l; m = -inf, l = 0 for an empty
+// split.
 __host__ __device__ inline int partial_stride(int rV_max, int d) {
   int s = 4 + rV_max + d;
   return (s + 3) & ~3;
@@ -118,26 +124,42 @@ struct DenseArgs {
 
 }  // namespace jolt
 
+// Global-memory views.  Pointers read from descriptors in memory are
+// generic, so without an explicit address space every access would compile
+// to a flat load (slower, and it couples the memory and LDS wait counters).
+// Native vector types keep small load buffers in registers.
+typedef uint32_t gu32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t gu32x2 __attribute__((ext_vector_type(2)));
+typedef float gf32x4 __attribute__((ext_vector_type(4)));
+template <typename T>
+using gptr = const __attribute__((address_space(1))) T *;
+template <typename T>
+__device__ inline gptr<T> gp(const void *p) {
+  return (gptr<T>)p;
+}
+
 // Copy rows of 16-byte chunks from global memory to LDS with every thread
-// keeping up to 8 loads in flight (a plain load-then-store loop would pay
-// one memory round trip per chunk).  src rows are src_cpr chunks long and
+// keeping 8 loads in flight (indices are clamped rather than branched on, so
+// the loads issue back to back).  src rows are src_cpr chunks long and
 // contiguous; dst rows start every dst_stride bytes.
-__device__ inline void stage_rows(uint8_t *dst, int dst_stride, const uint8_t *src, int rows,
+__device__ inline void stage_rows(uint8_t *dst, int dst_stride, const void *src, int rows,
                                   int src_cpr, int tid, int nthreads) {
   const int n = rows * src_cpr;
+  if (n <= 0) return;
+  gptr<gu32x4> g = gp<gu32x4>(src);
   for (int x0 = 0; x0 < n; x0 += 8 * nthreads) {
-    uint4 v[8];
+    gu32x4 v[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int x = x0 + k * nthreads + tid;
-      if (x < n) v[k] = ((const uint4 *)src)[x];
+      v[k] = g[x < n ? x : n - 1];
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int x = x0 + k * nthreads + tid;
       if (x < n) {
         const int r = x / src_cpr, c = x - r * src_cpr;
-        *(uint4 *)(dst + (size_t)r * dst_stride + 16 * c) = v[k];
+        *(gu32x4 *)(dst + (size_t)r * dst_stride + 16 * c) = v[k];
       }
     }
   }
@@ -148,6 +170,7 @@ hipError_t jolt_launch_generic(const jolt::DecodeArgs &a, int nseq, hipStream_t 
 hipError_t jolt_launch_mfma(const jolt::DecodeArgs &a, int nseq, int bK, int bV, int nkt,
                             int lds_bytes, hipStream_t s);
 hipError_t jolt_launch_merge(const jolt::DecodeArgs &a, int nseq, hipStream_t s);
+hipError_t jolt_launch_merge_outputs(const jolt::DecodeArgs &a, int nseq, hipStream_t s);
 hipError_t jolt_launch_dense(const jolt::DenseArgs &a, int nseq, hipStream_t s);
 hipError_t jolt_launch_dense_merge(const jolt::DenseArgs &a, int nseq, hipStream_t s);
 hipError_t jolt_launch_unpack(const jolt::LayerDev *layer, int tau, int H, int T, int d,

@@ -247,7 +247,7 @@ __device__ inline void split_columns(const float *pb, int st, int ns, const floa
       for (int k = 0; k < 16; ++k) v[k] = s0 + k < ns ? pb[(size_t)(s0 + k) * st + off0 + x] : 0.0f;
 #pragma unroll
       for (int k = 0; k < 16; ++k)
-        if (s0 + k < ns) acc += w_s[s0 + k] * v[k];
+        if (s0 + k < ns && w_s[s0 + k] > 0.0f) acc += w_s[s0 + k] * v[k];
     }
     dst[x] = acc * inv;
   }
@@ -381,17 +381,19 @@ __global__ __launch_bounds__(256) void dense_split(DenseArgs a) {
       if (t < t1) {
         size_t off = base + (size_t)t * D + 8 * li;
         if constexpr (KV32) {
-          const float4 *kp = (const float4 *)((const float *)a.k + off);
-          const float4 *vp = (const float4 *)((const float *)a.v + off);
-          float4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
-          kf[k][0] = k0.x; kf[k][1] = k0.y; kf[k][2] = k0.z; kf[k][3] = k0.w;
-          kf[k][4] = k1.x; kf[k][5] = k1.y; kf[k][6] = k1.z; kf[k][7] = k1.w;
-          vf[k][0] = v0.x; vf[k][1] = v0.y; vf[k][2] = v0.z; vf[k][3] = v0.w;
-          vf[k][4] = v1.x; vf[k][5] = v1.y; vf[k][6] = v1.z; vf[k][7] = v1.w;
+          gptr<gf32x4> kp = gp<gf32x4>(a.k), vp = gp<gf32x4>(a.v);
+          gf32x4 k0 = kp[off / 4], k1 = kp[off / 4 + 1], v0 = vp[off / 4], v1 = vp[off / 4 + 1];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kf[k][e] = k0[e];
+            kf[k][e + 4] = k1[e];
+            vf[k][e] = v0[e];
+            vf[k][e + 4] = v1[e];
+          }
         } else {
-          uint4 kk = *(const uint4 *)((const uint16_t *)a.k + off);
-          uint4 vv = *(const uint4 *)((const uint16_t *)a.v + off);
-          uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w}, vw[4] = {vv.x, vv.y, vv.z, vv.w};
+          gu32x4 kk = gp<gu32x4>(a.k)[off / 8];
+          gu32x4 vv = gp<gu32x4>(a.v)[off / 8];
+          uint32_t kw[4] = {kk[0], kk[1], kk[2], kk[3]}, vw[4] = {vv[0], vv[1], vv[2], vv[3]};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             kf[k][2 * e] = __uint_as_float(kw[e] << 16);
@@ -483,35 +485,65 @@ __global__ __launch_bounds__(256) void dense_split(DenseArgs a) {
       part[0] = mx;
       part[1] = ls;
     }
-    part[4 + f] = as;
+    part[4 + f] = ls > 0.0f ? as / ls : 0.0f;
   }
 }
 
-__global__ __launch_bounds__(128) void dense_merge(DenseArgs a) {
-  const int j = blockIdx.x, b = blockIdx.y, f = threadIdx.x, D = a.d, ns = a.n_split;
-  const int st = 4 + D;
-  const float *pb = a.ws + ((size_t)(b * a.H_q + j) * ns) * st;
-  __shared__ float w_s[kMaxSplits];
+// Combine split partials [m, l, 0, 0, o[d]] (o divided by its split's l) of
+// one (sequence, query head): o = sum_s w_s l_s o_s / sum_s w_s l_s with
+// w_s = exp(m_s - max m).  The first 32 splits' columns are fetched together
+// with m and l, so short reductions take one memory round trip.
+__global__ __launch_bounds__(256) void merge_outputs(const float *ws, float *out, int ns, int d,
+                                                     int H_q) {
+  const int j = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int st = 4 + d, f = tid & 127, part = tid >> 7;
+  const float *pb = ws + ((size_t)(b * H_q + j) * ns) * st;
+  __shared__ float m_s[kMaxSplits], w_s[kMaxSplits];
   __shared__ float red[8];
+  __shared__ float half_s[kMaxD];
+  float v[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int s = part + 2 * k;
+    v[k] = (f < d && s < ns) ? pb[(size_t)s * st + 4 + f] : 0.0f;
+  }
   float mx = -INFINITY;
-  for (int s = f; s < ns; s += 128) {
-    float m = pb[(size_t)s * st];
-    w_s[s] = m;
+  for (int s = tid; s < ns; s += 256) {
+    const float m = pb[(size_t)s * st], l = pb[(size_t)s * st + 1];
+    m_s[s] = m;
+    w_s[s] = l;
     mx = fmaxf(mx, m);
   }
   mx = block_reduce(mx, red, true);
   float ls = 0.0f;
-  for (int s = f; s < ns; s += 128) {
-    float m = w_s[s];
-    float w = m == -INFINITY ? 0.0f : __expf(m - mx);
+  for (int s = tid; s < ns; s += 256) {
+    const float m = m_s[s];
+    const float w = m == -INFINITY ? 0.0f : __expf(m - mx) * w_s[s];
     w_s[s] = w;
-    ls += w * pb[(size_t)s * st + 1];
+    ls += w;
   }
   ls = block_reduce(ls, red, false);
-  __shared__ float o_s[kMaxD];
-  split_columns(pb, st, ns, w_s, D, 4, 1.0f / ls, o_s, f, 128);
+  float acc = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int s = part + 2 * k;
+    if (s < ns && w_s[s] > 0.0f) acc += w_s[s] * v[k];  // empty splits carry no payload
+  }
+  for (int s0 = 32; s0 < ns; s0 += 32) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int s = s0 + part + 2 * k;
+      v[k] = (f < d && s < ns) ? pb[(size_t)s * st + 4 + f] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int s = s0 + part + 2 * k;
+      if (s < ns && w_s[s] > 0.0f) acc += w_s[s] * v[k];
+    }
+  }
+  if (part == 1 && f < d) half_s[f] = acc;
   __syncthreads();
-  if (f < D) a.out[((size_t)b * a.H_q + j) * D + f] = o_s[f];
+  if (part == 0 && f < d) out[((size_t)b * H_q + j) * d + f] = (acc + half_s[f]) / ls;
 }
 
 // ------------------------------------------------------------- unpack --
@@ -582,7 +614,14 @@ hipError_t jolt_launch_dense(const DenseArgs &a, int nseq, hipStream_t s) {
 }
 
 hipError_t jolt_launch_dense_merge(const DenseArgs &a, int nseq, hipStream_t s) {
-  hipLaunchKernelGGL(dense_merge, dim3(a.H_q, nseq), dim3(128), 0, s, a);
+  hipLaunchKernelGGL(merge_outputs, dim3(a.H_q, nseq), dim3(256), 0, s, (const float *)a.ws, a.out,
+                     a.n_split, a.d, a.H_q);
+  return hipGetLastError();
+}
+
+hipError_t jolt_launch_merge_outputs(const DecodeArgs &a, int nseq, hipStream_t s) {
+  hipLaunchKernelGGL(merge_outputs, dim3(a.H_q, nseq), dim3(256), 0, s, (const float *)a.ws, a.out,
+                     a.n_split, a.d, a.H_q);
   return hipGetLastError();
 }
 

@@ -109,7 +109,7 @@ typedef struct {
  * Errors: JOLT_E_INVALID (shape/rank/bits/NULL rules above, group_start not
  * strictly increasing from 0 to n_layers, n_q_heads not a multiple of
  * n_kv_heads, odd head_dim, T < 1), JOLT_E_UNSUPPORTED (head_dim not 64 or
- * 128, n_q_heads/n_kv_heads > 16), JOLT_E_OOM, JOLT_E_HIP.
+ * 128, n_q_heads/n_kv_heads > 16, T > 2^20), JOLT_E_OOM, JOLT_E_HIP.
  */
 jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream stream, jolt_cache **out);
 
@@ -132,14 +132,16 @@ jolt_status jolt_decode_workspace_size(const jolt_cache *const *caches, int32_t 
  * cache handle (handles in one call share n_layers, groups, heads and d; T
  * and the per-cell ranks and bits may differ).
  *   q         DEVICE [batch][n_q_heads][d], pre-RoPE, q_dtype (F32 or BF16)
- *   q_pos     HOST   [batch] query positions (normally the cache's T), >= 0
- *   inv_freq  HOST   [d/2] float32 RoPE inverse frequencies (any rope scaling
- *             already applied)
+ *   q_pos     HOST   [batch] query positions (normally the cache's T), in
+ *             [0, 2^20]
+ *   inv_freq  HOST   [d/2] float32 RoPE inverse frequencies in [0, 1] (any
+ *             rope scaling already applied)
  *   softmax_scale    multiplies q.k (normally 1/sqrt(d) x attention scaling)
  *   out       DEVICE [batch][n_q_heads][d] float32
  *   workspace DEVICE, >= jolt_decode_workspace_size bytes, caller-owned
  * Errors: JOLT_E_INVALID (NULL pointers, batch < 0, layer out of range,
- * handles with different shapes, q_pos < 0), JOLT_E_WORKSPACE,
+ * handles with different shapes, q_pos or inv_freq out of range),
+ * JOLT_E_WORKSPACE,
  * JOLT_E_UNSUPPORTED (kernel forced to MFMA for a cache it cannot run),
  * JOLT_E_HIP.  batch == 0 is a no-op.
  */
@@ -159,8 +161,8 @@ jolt_status jolt_dense_workspace_size(int32_t batch, int32_t n_kv, int32_t n_q, 
  *   k_rope, v  DEVICE [batch][n_kv][T][d] in kv_dtype (F32 or BF16); keys
  *              already rotated to their positions 0..T-1
  *   q, q_pos, inv_freq, softmax_scale, out, workspace: as jolt_decode_attention
- * Errors: JOLT_E_INVALID, JOLT_E_UNSUPPORTED (d not 64/128, n_q/n_kv > 16),
- * JOLT_E_WORKSPACE, JOLT_E_HIP.
+ * Errors: JOLT_E_INVALID, JOLT_E_UNSUPPORTED (d not 64/128, n_q/n_kv > 16,
+ * T > 2^20), JOLT_E_WORKSPACE, JOLT_E_HIP.
  */
 jolt_status jolt_dense_attention(const void *k_rope, const void *v, jolt_dtype kv_dtype,
                                  int32_t batch, int32_t n_kv, int32_t n_q, int32_t d, int32_t T,

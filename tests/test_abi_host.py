@@ -141,3 +141,13 @@ def test_dense_validation(args, status):
 def test_dense_workspace_size_formula():
     n = J.jolt_dense_workspace_size(2, 8, 32, 128, 4096, split_tokens=256)
     assert n == 2 * 32 * (4096 // 256) * (4 + 128) * 4
+
+
+def test_rope_domain_checked_before_launch():
+    # positions above 2^20 or frequencies above 1 are rejected on the host
+    assert J.jolt_decode_workspace_size([], 0) == 0
+    expect(-1, J.jolt_debug_sincos, np.array([2.0 ** 21], np.float32), match="2\\^20")
+
+
+def test_long_context_rejected_at_load():
+    expect(-2, J.jolt_load_cache, mutate(T=(1 << 20) + 1), 0, match="T=")

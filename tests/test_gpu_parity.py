@@ -283,8 +283,9 @@ def test_rope_sincos_accuracy():
         sn, cs = J.jolt_debug_sincos(ang)
         a64 = ang.astype(np.float64)
         worst = max(worst, np.max(np.abs(sn - np.sin(a64))), np.max(np.abs(cs - np.cos(a64))))
-    # large arguments take the library path
-    big = np.array([1048576.0, 3.0e6, -2.5e6], dtype=np.float32)
+    # the whole domain of the reduction: random float32 angles below 2^20
+    big = (np.random.default_rng(0).random(200000) * 2 - 1).astype(np.float32) * np.float32(1048575.0)
     sn, cs = J.jolt_debug_sincos(big)
-    worst = max(worst, np.max(np.abs(sn - np.sin(big.astype(np.float64)))))
+    b64 = big.astype(np.float64)
+    worst = max(worst, np.max(np.abs(sn - np.sin(b64))), np.max(np.abs(cs - np.cos(b64))))
     assert worst <= 4e-7, worst
