@@ -178,7 +178,7 @@ def main():
     split = args.split_tokens
     ws_bytes = max(J.jolt_decode_workspace_size(caches[0], l, kernel=kernel, split_tokens=split)
                    for l in range(L))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     ev = HipEvents()
     n_ev = args.steps * L
     evb, eve = ev.create(n_ev), ev.create(n_ev)
@@ -233,7 +233,7 @@ def main():
                 torch.randn((B, H, T, d), generator=g, device=dev).to(torch.bfloat16))
                for _ in range(L)] for _ in range(dcopies)]
         dsplit = args.dense_split_tokens
-        dws = torch.empty(J.jolt_dense_workspace_size(B, H, Hq, d, T, split_tokens=dsplit),
+        dws = torch.zeros(J.jolt_dense_workspace_size(B, H, Hq, d, T, split_tokens=dsplit),
                           dtype=torch.uint8, device=dev)
 
         def dstep(i):

@@ -72,7 +72,7 @@ static inline float bf16_to_f32(uint16_t h) {
 
 // --------------------------------------------------------- cache handle --
 struct CellMeta {
-  int rT, rF, bits, rT_pad, rF_pad, kw;
+  int rT, rF, bits, rT_pad, rF_pad;
 };
 
 struct jolt_cache {
@@ -206,9 +206,11 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
       for (int c2 = 0; c2 < d; ++c2)
         ((_Float16 *)(S.buf.data() + off_pih))[(size_t)r * d + c2] =
             (_Float16)Pi64[(size_t)r * d + (c2 & ~31) + perm32(c2 & 31)];
+    size_t off_pik = S.take(sizeof(_Float16) * d * d);
+    for (int i = 0; i < d * d; ++i) ((_Float16 *)(S.buf.data() + off_pik))[i] = (_Float16)Pi64[i];
 
     struct Offs {
-      size_t A, B, Bt, W;
+      size_t A, B, Bt;
       std::vector<size_t> G, W2, codes, scales;  // per layer in group
     };
     std::vector<Offs> offs(2 * c->n_groups);
@@ -223,7 +225,6 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
         m.bits = in.bits;
         m.rT_pad = round_up(in.r_T, kRankPad);
         m.rF_pad = round_up(in.r_F, kRankPad);
-        m.kw = m.rF_pad + (in.bits > 0 ? d : 0);
         c->cells[2 * g + tau] = m;
         Offs &o = offs[2 * g + tau];
         // A
@@ -246,22 +247,6 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
           for (int j = 0; j < m.rF; ++j)
             ((float *)(S.buf.data() + o.Bt))[(size_t)j * d + f] =
                 load_factor(in.B, (size_t)f * m.rF + j, f32);
-        // W = [B_K (slot-permuted) | Pi] in fp16, keys of bf16 caches only
-        o.W = 0;
-        if (tau == 0 && !f32) {
-          o.W = S.take(sizeof(_Float16) * d * m.kw);
-          _Float16 *W = (_Float16 *)(S.buf.data() + o.W);
-          for (int f = 0; f < d; ++f) {
-            for (int col = 0; col < m.rF_pad; ++col) {
-              int j = (col & ~31) + perm32(col & 31);
-              float v = j < m.rF ? load_factor(in.B, (size_t)f * m.rF + j, false) : 0.0f;
-              W[(size_t)f * m.kw + col] = (_Float16)v;
-            }
-            if (m.bits > 0)
-              for (int i = 0; i < d; ++i)
-                W[(size_t)f * m.kw + m.rF_pad + i] = (_Float16)Pi64[(size_t)f * d + i];
-          }
-        }
         // G and residual, per layer of the group
         for (int lp = 0; lp < gs; ++lp) {
           size_t og = S.take((size_t)fb * H * std::max(m.rT_pad, 1) * std::max(m.rF_pad, 1));
@@ -274,8 +259,8 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
                                       : ((size_t)h * m.rT_pad + r) * m.rF_pad + j;
                 store_factor(S.buf.data() + og, dst, in.G, src, f32);
               }
-          // value finalize matrix W2[h] = B_V G_V[lp, h]^T (bf16 caches)
-          if (tau == 1 && !f32 && m.rT > 0) {
+          // W2[h] = B G[lp, h]^T (bf16 caches): key-tile and value-finalize matrix
+          if (!f32 && m.rT > 0) {
             size_t ow = S.take(sizeof(_Float16) * H * d * m.rT_pad);
             o.W2.push_back(ow);
             _Float16 *W2 = (_Float16 *)(S.buf.data() + ow);
@@ -286,7 +271,7 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
                 Gf[i] = load_factor(in.G, ((size_t)lp * H + hh) * m.rT * m.rF + i, false);
               for (int f = 0; f < d; ++f)
                 for (int col = 0; col < m.rT_pad; ++col) {
-                  int r = (col & ~31) + perm32(col & 31);
+                  int r = tau == 1 ? (col & ~31) + perm32(col & 31) : col;
                   double acc = 0.0;
                   if (r < m.rT)
                     for (int j = 0; j < m.rF; ++j) acc += Bf[(size_t)f * m.rF + j] * Gf[(size_t)r * m.rF + j];
@@ -348,6 +333,7 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
       L.Pi = (const float *)(base + off_pi);
       L.PiT = (const float *)(base + off_pit);
       L.PiH = (const _Float16 *)(base + off_pih);
+      L.PiK = (const _Float16 *)(base + off_pik);
       L.T = T;
       L.T_pad = T_pad;
       L.f32 = f32 ? 1 : 0;
@@ -359,7 +345,6 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
         cd.B = base + o.B;
         cd.Bt = (const float *)(base + o.Bt);
         cd.G = base + o.G[lp];
-        cd.W = o.W ? (const _Float16 *)(base + o.W) : nullptr;
         cd.W2 = o.W2[lp] ? (const _Float16 *)(base + o.W2[lp]) : nullptr;
         cd.codes = m.bits ? base + o.codes[lp] : nullptr;
         cd.scales = m.bits ? (const float *)(base + o.scales[lp]) : nullptr;
@@ -368,7 +353,6 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
         cd.bits = m.bits;
         cd.rT_pad = m.rT_pad;
         cd.rF_pad = m.rF_pad;
-        cd.kw = m.kw;
       }
     }
     std::memcpy(S.buf.data() + off_layers, c->h_layers.data(), sizeof(LayerDev) * c->n_layers);
@@ -419,19 +403,23 @@ struct Plan {
   size_t ws_bytes;
 };
 
-// The MFMA kernel stages G_K[h]^T and W = [B_K | Pi] in LDS (rows padded by
-// 8 elements) next to 8.5 KiB of exchange buffers, 8 KiB of rotated
-// queries and the epilogue's exchange of the value partials, prefetches up to 256 key ranks a tile ahead in registers and keeps
-// the value-rank accumulators of up to 512 ranks in registers.
+// The MFMA kernel stages W2_K[h] = B_K G_K[h]^T and (with a key residual)
+// Pi in LDS as fp16 rows padded by 8 elements, next to 8.5 KiB of exchange
+// buffers, 8 KiB of rotated queries and the epilogue's exchange of the value
+// partials; key ranks up to 256 are prefetched a tile ahead in registers and
+// value ranks up to 512 accumulate in registers.
+static int mfma_lds_bytes(const CellDev &k, const CellDev &v, int d) {
+  return 2 * d * (k.rT_pad + 8) + (k.bits > 0 ? 2 * d * (d + 8) : 0) + 8704 + 16 * 128 * 4 +
+         512 * (v.rT_pad / 16 + 8);
+}
+
 static bool mfma_ok(const jolt_cache *c, int layer, int *lds) {
   if (c->f32 || c->d != 128) return false;
   const LayerDev &L = c->h_layers[layer];
   const CellDev &k = L.c[0], &v = L.c[1];
   if (v.rT_pad > 512 || k.rT_pad > 256) return false;
-  int bytes = 2 * k.rF_pad * (k.rT_pad + 8) + 2 * c->d * (k.kw + 8) + 8704 + 16 * 128 * 4 +
-              512 * (v.rT_pad / 16 + 8);
-  *lds = bytes;
-  return bytes <= jolt_mfma_max_lds();
+  *lds = mfma_lds_bytes(k, v, c->d);
+  return *lds <= jolt_mfma_max_lds();
 }
 
 static jolt_status plan_decode(const jolt_cache *const *caches, int batch, int layer,

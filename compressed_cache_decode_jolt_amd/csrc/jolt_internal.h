@@ -55,9 +55,11 @@ struct CellDev {
   const void *G;
   const void *B;          // [d][rF_pad], factor dtype
   const float *Bt;        // V: B^T as float32, [rF_pad][d] (finalize reads)
-  const _Float16 *W;      // K, bf16 caches: [d][kw] fp16 = [B_K | Pi] (see host)
-  // V, bf16 caches: W2 = B_V G_V[h]^T of this layer, [H][d][rT_pad] fp16,
-  // columns in perm32 order inside each 32-block (finalize on MFMA)
+  // bf16 caches: W2 = B G[h]^T of this layer, [H][d][rT_pad] fp16 -- the
+  // key tile is rebuilt as W2_K A_K^T in one MFMA chain; for values it
+  // finalizes the split partials.  Value columns are in perm32 order inside
+  // each 32-block (they multiply result tiles), key columns in rank order
+  // (they multiply A_K rows read straight from memory).
   const _Float16 *W2;
   // Residual codes of this layer.
   // K: [H][T_pad][d*b/8]; a row is 4 chunks (one per 16-lane group g) of
@@ -67,7 +69,7 @@ struct CellDev {
   //    slots q = 0..31 (token perm32(q)) in code_pos order.
   const uint8_t *codes;
   const float *scales;    // this layer: [H][T_pad]
-  int32_t rT, rF, bits, rT_pad, rF_pad, kw;
+  int32_t rT, rF, bits, rT_pad, rF_pad;
 };
 
 struct LayerDev {
@@ -75,6 +77,7 @@ struct LayerDev {
   const float *Pi;        // [d][d] float32, row-major
   const float *PiT;       // Pi^T, [d][d] float32 (finalize reads)
   const _Float16 *PiH;    // Pi in fp16, [d][d], columns perm32 inside 32-blocks
+  const _Float16 *PiK;    // Pi in fp16, [d][d], natural column order
   int32_t T, T_pad, f32;  // f32: factors stored as float32 (else bf16)
 };
 

@@ -489,6 +489,178 @@ __global__ __launch_bounds__(256) void dense_split(DenseArgs a) {
   }
 }
 
+// Flash-decoding over bf16 post-RoPE K and V with the scores on MFMA.
+// Each wave takes 16 tokens per step: S^T (16 tokens x 16 query slots) =
+// K Q^T on v_mfma_f32_16x16x32_bf16, K rows feeding the A operand straight
+// from memory and the rotated query split into bf16 high and low parts (two
+// products) so the scores carry ~16 mantissa bits of q.  The wave keeps its
+// own online-softmax state; p goes through LDS to the lanes that own two
+// output features each, which accumulate p V on VALU.  The next step's K and
+// V are in flight while the current one is computed.
+typedef __bf16 bf16x8d __attribute__((ext_vector_type(8)));
+typedef float f32x4d __attribute__((ext_vector_type(4)));
+
+template <int D, int HG>
+__global__ __launch_bounds__(256, 2) void dense_mfma(DenseArgs a) {
+  constexpr int KS = D / 32;          // K-steps of the score product
+  constexpr int FPL = D / 64;         // output features per lane
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int Hg = a.Hg, T = a.T;
+  const int t0 = split * a.split_tokens, t1 = min(T, t0 + a.split_tokens);
+  __shared__ float qs[16][D];
+  __shared__ float Pw[4][16][17];      // per wave: [token][query], padded
+  __shared__ float Aw[4][16];          // per wave: rescale factor per query
+  __shared__ float Mw[4][16], Lw[4][16];
+  __shared__ float Ow[4][HG][D];
+
+  for (int x = tid; x < 16 * (D / 2); x += 256) {
+    const int u = x / (D / 2), i = x % (D / 2);
+    float lo = 0.0f, hi = 0.0f;
+    if (u < Hg) {
+      const size_t qi = ((size_t)b * a.H_q + h * Hg + u) * D;
+      float c, sn;
+      rope_cs(a.q_pos[b], a.inv_freq[i], &c, &sn);
+      const float xl = ldq(a.q, qi + i, a.q_f32), xh = ldq(a.q, qi + i + D / 2, a.q_f32);
+      lo = (xl * c - xh * sn) * a.scale;
+      hi = (xh * c + xl * sn) * a.scale;
+    }
+    qs[u][i] = lo;
+    qs[u][i + D / 2] = hi;
+  }
+  __syncthreads();
+  bf16x8d qh[KS], ql[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float x = qs[lr][32 * s + 8 * lg + j];
+      const __bf16 hb = (__bf16)x;
+      qh[s][j] = hb;
+      ql[s][j] = (__bf16)(x - (float)hb);
+    }
+
+  gptr<bf16x8d> Kp = gp<bf16x8d>(a.k);
+  gptr<uint32_t> Vp = gp<uint32_t>(a.v);
+  const size_t base = ((size_t)b * a.H + h) * T;  // token rows of this head
+  float m_w = -INFINITY, l_w = 0.0f;
+  float acc[HG][FPL];
+#pragma unroll
+  for (int u = 0; u < HG; ++u)
+#pragma unroll
+    for (int e = 0; e < FPL; ++e) acc[u][e] = 0.0f;
+
+  auto fetch = [&](int tb, bf16x8d (&kf)[KS], uint32_t (&vf)[16]) {
+    const int tk = min(tb + lr, T - 1);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kf[s] = Kp[(base + tk) * (D / 8) + 4 * s + lg];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int tv = min(tb + t, T - 1);
+      if constexpr (FPL == 2)
+        vf[t] = Vp[(base + tv) * (D / 2) + lane];
+      else
+        vf[t] = (uint32_t)gp<uint16_t>(a.v)[(base + tv) * D + lane];
+    }
+  };
+  bf16x8d kf[KS];
+  uint32_t vf[16];
+  int tb = t0 + 16 * wave;
+  if (tb < t1) fetch(tb, kf, vf);
+  for (int it = t0; it < t1; it += 64, tb += 64) {
+    const bool live = tb < t1;
+    bf16x8d kc[KS];
+    uint32_t vc[16];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kc[s] = kf[s];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) vc[t] = vf[t];
+    if (tb + 64 < t1) fetch(tb + 64, kf, vf);
+    float p[4] = {0, 0, 0, 0}, alpha = 1.0f;
+    if (live) {
+      f32x4d sacc = {0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc[s], qh[s], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc[s], ql[s], sacc, 0, 0, 0);
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (tb + 4 * lg + i >= t1) sacc[i] = -INFINITY;
+        mx = fmaxf(mx, sacc[i]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m_w, mx);
+      alpha = __expf(m_w - mn);
+      m_w = mn;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __expf(sacc[i] - mn);
+        l_w = (i == 0 ? alpha * l_w : l_w) + p[i];
+        Pw[wave][4 * lg + i][lr] = p[i];
+      }
+      if (lg == 0) Aw[wave][lr] = alpha;
+    }
+    __syncthreads();
+    if (live) {
+#pragma unroll
+      for (int u = 0; u < HG; ++u) {
+        const float al = Aw[wave][u];
+#pragma unroll
+        for (int e = 0; e < FPL; ++e) acc[u][e] *= al;
+      }
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        float v0, v1 = 0.0f;
+        if constexpr (FPL == 2) {
+          v0 = __uint_as_float(vc[t] << 16);
+          v1 = __uint_as_float(vc[t] & 0xffff0000u);
+        } else {
+          v0 = __uint_as_float(vc[t] << 16);
+        }
+#pragma unroll
+        for (int u = 0; u < HG; ++u) {
+          const float pu = Pw[wave][t][u];
+          acc[u][0] += pu * v0;
+          if constexpr (FPL == 2) acc[u][1] += pu * v1;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // combine the waves
+  l_w += __shfl_xor(l_w, 16);
+  l_w += __shfl_xor(l_w, 32);
+  if (lg == 0) {
+    Mw[wave][lr] = m_w;
+    Lw[wave][lr] = l_w;
+  }
+#pragma unroll
+  for (int u = 0; u < HG; ++u)
+#pragma unroll
+    for (int e = 0; e < FPL; ++e) Ow[wave][u][FPL * lane + e] = acc[u][e];
+  __syncthreads();
+  for (int x = tid; x < Hg * D; x += 256) {
+    const int u = x / D, f = x % D;
+    float mx = fmaxf(fmaxf(Mw[0][u], Mw[1][u]), fmaxf(Mw[2][u], Mw[3][u]));
+    float ls = 0.0f, os = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float wt = Mw[w][u] == -INFINITY ? 0.0f : __expf(Mw[w][u] - mx);
+      ls += wt * Lw[w][u];
+      os += wt * Ow[w][u][f];
+    }
+    float *part = a.ws + ((size_t)(b * a.H_q + h * Hg + u) * a.n_split + split) * (4 + D);
+    if (f == 0) {
+      part[0] = mx;
+      part[1] = ls;
+    }
+    part[4 + f] = ls > 0.0f ? os / ls : 0.0f;
+  }
+}
+
 // Combine split partials [m, l, 0, 0, o[d]] (o divided by its split's l) of
 // one (sequence, query head): o = sum_s w_s l_s o_s / sum_s w_s l_s with
 // w_s = exp(m_s - max m).  The first 32 splits' columns are fetched together
@@ -604,8 +776,25 @@ static void launch_dense_hg(const DenseArgs &a, dim3 grid, hipStream_t s) {
     hipLaunchKernelGGL((dense_split<D, 16, KV32>), grid, dim3(256), 0, s, a);
 }
 
+template <int D>
+static void launch_dense_mfma(const DenseArgs &a, dim3 grid, hipStream_t s) {
+  if (a.Hg <= 4)
+    hipLaunchKernelGGL((dense_mfma<D, 4>), grid, dim3(256), 0, s, a);
+  else if (a.Hg <= 8)
+    hipLaunchKernelGGL((dense_mfma<D, 8>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((dense_mfma<D, 16>), grid, dim3(256), 0, s, a);
+}
+
 hipError_t jolt_launch_dense(const DenseArgs &a, int nseq, hipStream_t s) {
   dim3 grid(a.n_split, a.H, nseq);
+  if (!a.kv_f32) {
+    if (a.d == 128)
+      launch_dense_mfma<128>(a, grid, s);
+    else
+      launch_dense_mfma<64>(a, grid, s);
+    return hipGetLastError();
+  }
   if (a.d == 128)
     a.kv_f32 ? launch_dense_hg<128, true>(a, grid, s) : launch_dense_hg<128, false>(a, grid, s);
   else

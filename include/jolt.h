@@ -138,7 +138,9 @@ jolt_status jolt_decode_workspace_size(const jolt_cache *const *caches, int32_t 
  *             rope scaling already applied)
  *   softmax_scale    multiplies q.k (normally 1/sqrt(d) x attention scaling)
  *   out       DEVICE [batch][n_q_heads][d] float32
- *   workspace DEVICE, >= jolt_decode_workspace_size bytes, caller-owned
+ *   workspace DEVICE, >= jolt_decode_workspace_size bytes, caller-owned;
+ *             needs no initialisation; one workspace serves one call at a
+ *             time (stream order).
  * Errors: JOLT_E_INVALID (NULL pointers, batch < 0, layer out of range,
  * handles with different shapes, q_pos or inv_freq out of range),
  * JOLT_E_WORKSPACE,

@@ -37,13 +37,15 @@ def rel_l2(a, b):
 
 
 def run_decode(caches, layer, q, q_pos, inv, scale, q_dtype="bf16", kernel=None, split=0,
-               handles=None):
+               handles=None, ws=None):
     hs = handles or [J.jolt_load_cache(c) for c in caches]
     dt = torch.bfloat16 if q_dtype == "bf16" else torch.float32
     qt = torch.from_numpy(np.asarray(q, dtype=np.float32)).to(dt).cuda()
     out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
     nb = J.jolt_decode_workspace_size(hs, layer, kernel=kernel, split_tokens=split)
-    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    if ws is None:
+        ws = torch.zeros(max(nb, 1), dtype=torch.uint8, device="cuda")
+    assert ws.numel() >= nb
     J.jolt_decode_attention(hs, layer, qt, q_pos, inv, scale, out, ws, kernel=kernel,
                             split_tokens=split)
     torch.cuda.synchronize()
@@ -209,6 +211,35 @@ def test_batch_of_different_lengths_and_ranks(kernel):
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
+def test_workspace_reused_across_calls(kernel):
+    """One workspace, never cleared, serves consecutive calls with different
+    shapes and split counts (stale partials of a longer call must not leak
+    into a shorter one)."""
+    d, H, H_q = 128, 4, 16
+    ws = torch.full((1 << 22,), 0x7F, dtype=torch.uint8, device="cuda")
+    inv = gen.rope_inv_freq_input(5e5, d)
+    for i, (T, split) in enumerate([(700, 128), (2000, 256), (300, 0), (700, 128)]):
+        c = gen.small_cache(70 + i, T, H, H_q, d, [((32, 32, 4), (64, 32, 2))], [1])
+        q = gen.queries(84, i, 0, H_q, d, "bf16")[None]
+        got = run_decode([c], 0, q, [T], inv, 0.1, kernel=kernel, split=split, ws=ws)
+        want = oracle_decode([c], 0, q, [T], inv, 0.1)
+        assert rel_l2(got, want) <= tol(kernel, False)[0], (i, rel_l2(got, want))
+    # dense path on the same workspace
+    g = np.random.default_rng(5)
+    K = gen.to_bf16_values(g.standard_normal((1, H, 500, d))).astype(np.float64)
+    V = gen.to_bf16_values(g.standard_normal((1, H, 500, d))).astype(np.float64)
+    for _ in range(2):
+        out = torch.empty((1, H_q, d), dtype=torch.float32, device="cuda")
+        J.jolt_dense_attention(torch.from_numpy(K.astype(np.float32)).to(torch.bfloat16).cuda(),
+                               torch.from_numpy(V.astype(np.float32)).to(torch.bfloat16).cuda(),
+                               torch.from_numpy(q.astype(np.float32)).to(torch.bfloat16).cuda(),
+                               [500], inv, 0.1, out, ws, split_tokens=64)
+        torch.cuda.synchronize()
+        want = att.dense_attention(K, V, q.astype(np.float64), [500], inv, 0.1)
+        assert rel_l2(out.cpu().numpy(), want) <= 1e-5
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
 def test_layer_groups(kernel):
     d, H, H_q, T = 128, 2, 8, 200
     c = gen.small_cache(30, T, H, H_q, d, [((32, 16, 4), (64, 32, 2)), ((16, 16, 8), (16, 32, 0))],
@@ -264,7 +295,7 @@ def test_dense_parity(d, H, H_q, T, kv):
     vt = torch.from_numpy(V.astype(np.float32)).to(dt).cuda()
     qt = torch.from_numpy(q.astype(np.float32)).to(torch.bfloat16).cuda()
     out = torch.empty((2, H_q, d), dtype=torch.float32, device="cuda")
-    ws = torch.empty(J.jolt_dense_workspace_size(2, H, H_q, d, T), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(J.jolt_dense_workspace_size(2, H, H_q, d, T), dtype=torch.uint8, device="cuda")
     J.jolt_dense_attention(kt, vt, qt, [T, T + 5], inv, 1 / math.sqrt(d), out, ws)
     torch.cuda.synchronize()
     want = att.dense_attention(K, V, q, [T, T + 5], inv, 1 / math.sqrt(d))
