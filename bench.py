@@ -14,7 +14,6 @@ the dense decode comparator on the same shape and the CPU oracle baseline.
 """
 import argparse
 import ctypes as C
-import hashlib
 import json
 import math
 import os
@@ -81,15 +80,6 @@ def algorithmic(cfg, alloc, layer):
     return nbytes, flops
 
 
-def kernel_hash():
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "compressed_cache_decode_jolt_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(workload, kernel_name):
     """HBM bytes per launch from the committed rocprofv3 counter runs, only if
     the kernel sources are unchanged since the counters were taken."""
@@ -97,6 +87,7 @@ def measured_traffic(workload, kernel_name):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(f"{workload}/{kernel_name}")
+    from compressed_cache_decode_jolt_amd.profiling import kernel_hash
     if not rec or rec.get("kernel_hash") != kernel_hash():
         return None
     return rec["bytes_per_launch"]
@@ -146,6 +137,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build measures the single-GPU decode path "
@@ -155,6 +148,16 @@ def main():
     import torch
     import compressed_cache_decode_jolt_amd as J
     from workloads import gen, get_config
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n}))
+        return
 
     cfg = get_config(args.config)
     ratio_key, alloc = load_alloc(cfg, args.ratio)
@@ -209,7 +212,8 @@ def main():
     bytes_launch = B * float(np.mean([p[0] for p in per_launch]))
     flops_launch = B * float(np.mean([p[1] for p in per_launch]))
     mfma_bound = flops_launch / PEAK_MFMA_BF16 > bytes_launch / PEAK_HBM
-    kname = "decode_split"
+    kname = ("decode_mfma" if args.kernel != "generic" and cfg.factor_dtype == "bf16" and d == 128
+             else "decode_generic")
     if mfma_bound:
         achieved = flops_launch / (kern_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_BF16 / 1e12,
