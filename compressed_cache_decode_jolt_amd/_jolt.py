@@ -63,7 +63,7 @@ EXPORTS = {
     "jolt_last_error": (C.c_char_p, []),
     "jolt_make_rotation": (C.c_int, [C.c_uint64, C.c_int32, C.POINTER(C.c_double)]),
     "jolt_debug_unpack": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
-    "jolt_debug_sincos": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p]),
+    "jolt_debug_sincos": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32]),
 }
 
 
@@ -262,8 +262,9 @@ def jolt_debug_unpack(cache, layer, tau, stream=None):
     return out
 
 
-def jolt_debug_sincos(angles):
+def jolt_debug_sincos(angles, variant=0):
     x = np.ascontiguousarray(angles, dtype=np.float32)
     sn, cs = np.empty_like(x), np.empty_like(x)
-    _check(lib().jolt_debug_sincos(x.ctypes.data, x.size, sn.ctypes.data, cs.ctypes.data))
+    _check(lib().jolt_debug_sincos(x.ctypes.data, x.size, sn.ctypes.data, cs.ctypes.data,
+                                   int(variant)))
     return sn, cs

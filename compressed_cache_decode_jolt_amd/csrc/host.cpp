@@ -73,6 +73,7 @@ static inline float bf16_to_f32(uint16_t h) {
 // --------------------------------------------------------- cache handle --
 struct CellMeta {
   int rT, rF, bits, rT_pad, rF_pad;
+  double a_s;  // keys of bf16 caches: A stored as fp16(A * a_s)
 };
 
 struct jolt_cache {
@@ -227,14 +228,33 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
         m.rF_pad = round_up(in.r_F, kRankPad);
         c->cells[2 * g + tau] = m;
         Offs &o = offs[2 * g + tau];
-        // A
+        // A.  Keys of bf16 caches: fp16 scaled by a power of two a_s (exact
+        // for every bf16 value in fp16's normal range) so that the key tile's
+        // MFMA takes A_K rows as they are; W2_K carries the 1 / a_s.
         o.A = S.take((size_t)fb * T_pad * std::max(m.rT_pad, 1));
+        m.a_s = 1.0;
+        const bool a16 = tau == 0 && !f32;
+        if (a16) {
+          float amax = 0.0f;
+          for (size_t i = 0; i < (size_t)T * m.rT; ++i)
+            amax = std::max(amax, std::fabs(load_factor(in.A, i, false)));
+          if (amax > 0.0f) {
+            int E;
+            std::frexp(amax, &E);  // amax in [2^(E-1), 2^E)
+            m.a_s = std::ldexp(1.0, 8 - E);
+          }
+        }
         for (int t = 0; t < T; ++t)
           for (int r = 0; r < m.rT; ++r) {
             size_t dst = tau == 0 ? (size_t)t * m.rT_pad + r
                                   : (size_t)r * T_pad + (t & ~31) + perm32_inv(t & 31);
-            store_factor(S.buf.data() + o.A, dst, in.A, (size_t)t * m.rT + r, f32);
+            if (a16)
+              ((_Float16 *)(S.buf.data() + o.A))[dst] =
+                  (_Float16)(load_factor(in.A, (size_t)t * m.rT + r, false) * (float)m.a_s);
+            else
+              store_factor(S.buf.data() + o.A, dst, in.A, (size_t)t * m.rT + r, f32);
           }
+        c->cells[2 * g + tau].a_s = m.a_s;
         // B
         o.B = S.take((size_t)fb * d * std::max(m.rF_pad, 1));
         for (int f = 0; f < d; ++f)
@@ -259,9 +279,11 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
                                       : ((size_t)h * m.rT_pad + r) * m.rF_pad + j;
                 store_factor(S.buf.data() + og, dst, in.G, src, f32);
               }
-          // W2[h] = B G[lp, h]^T (bf16 caches): key-tile and value-finalize matrix
+          // W2[h] = B G[lp, h]^T (bf16 caches): key-tile matrix (divided by
+          // a_s, the scale of the fp16 A_K) and value-finalize matrix, fp16,
+          // formed in float64 and rounded once
           if (!f32 && m.rT > 0) {
-            size_t ow = S.take(sizeof(_Float16) * H * d * m.rT_pad);
+            size_t ow = S.take(sizeof(uint16_t) * H * d * m.rT_pad);
             o.W2.push_back(ow);
             _Float16 *W2 = (_Float16 *)(S.buf.data() + ow);
             std::vector<double> Bf((size_t)d * m.rF), Gf((size_t)m.rT * m.rF);
@@ -275,7 +297,7 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
                   double acc = 0.0;
                   if (r < m.rT)
                     for (int j = 0; j < m.rF; ++j) acc += Bf[(size_t)f * m.rF + j] * Gf[(size_t)r * m.rF + j];
-                  W2[((size_t)hh * d + f) * m.rT_pad + col] = (_Float16)acc;
+                  W2[((size_t)hh * d + f) * m.rT_pad + col] = (_Float16)(acc / m.a_s);
                 }
             }
           } else {
@@ -345,7 +367,7 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
         cd.B = base + o.B;
         cd.Bt = (const float *)(base + o.Bt);
         cd.G = base + o.G[lp];
-        cd.W2 = o.W2[lp] ? (const _Float16 *)(base + o.W2[lp]) : nullptr;
+        cd.W2 = o.W2[lp] ? (const void *)(base + o.W2[lp]) : nullptr;
         cd.codes = m.bits ? base + o.codes[lp] : nullptr;
         cd.scales = m.bits ? (const float *)(base + o.scales[lp]) : nullptr;
         cd.rT = m.rT;
@@ -353,6 +375,7 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
         cd.bits = m.bits;
         cd.rT_pad = m.rT_pad;
         cd.rF_pad = m.rF_pad;
+        cd.a_inv = (float)(1.0 / m.a_s);
       }
     }
     std::memcpy(S.buf.data() + off_layers, c->h_layers.data(), sizeof(LayerDev) * c->n_layers);
@@ -668,9 +691,10 @@ extern "C" jolt_status jolt_debug_unpack(const jolt_cache *c, int32_t layer, int
 }
 
 extern "C" jolt_status jolt_debug_sincos(const float *angles, int32_t n, float *sin_out,
-                                         float *cos_out) {
+                                         float *cos_out, int32_t variant) {
   if (n < 0 || (n > 0 && (!angles || !sin_out || !cos_out)))
     return fail(JOLT_E_INVALID, "NULL argument or n < 0");
+  if (variant != 0 && variant != 1) return fail(JOLT_E_INVALID, "variant %d not 0 or 1", variant);
   for (int i = 0; i < n; ++i)
     if (!(std::fabs(angles[i]) < (float)kMaxPos))
       return fail(JOLT_E_INVALID, "angle %g outside (-2^20, 2^20)", (double)angles[i]);
@@ -678,7 +702,7 @@ extern "C" jolt_status jolt_debug_sincos(const float *angles, int32_t n, float *
   float *d = nullptr;
   HIP_TRY(hipMalloc(&d, sizeof(float) * 3 * (size_t)n));
   hipError_t e = hipMemcpy(d, angles, sizeof(float) * n, hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = jolt_launch_sincos(d, n, d + n, d + 2 * (size_t)n, nullptr);
+  if (e == hipSuccess) e = jolt_launch_sincos(d, n, d + n, d + 2 * (size_t)n, variant, nullptr);
   if (e == hipSuccess) e = hipMemcpy(sin_out, d + n, sizeof(float) * n, hipMemcpyDeviceToHost);
   if (e == hipSuccess) e = hipMemcpy(cos_out, d + 2 * (size_t)n, sizeof(float) * n, hipMemcpyDeviceToHost);
   hipFree(d);

@@ -47,7 +47,7 @@ __host__ __device__ inline void code_pos(int q, int bits, int *dword, int *shift
 }
 
 struct CellDev {
-  // K: A [T_pad][rT_pad] row-major.
+  // K: A [T_pad][rT_pad] row-major (fp16, scaled, for bf16 caches).
   // V: A^T [rT_pad][T_pad], tokens in perm32 order inside 32-token blocks.
   const void *A;
   // K: G^T of this layer, [H][rF_pad][rT_pad].  V: G of this layer,
@@ -55,12 +55,12 @@ struct CellDev {
   const void *G;
   const void *B;          // [d][rF_pad], factor dtype
   const float *Bt;        // V: B^T as float32, [rF_pad][d] (finalize reads)
-  // bf16 caches: W2 = B G[h]^T of this layer, [H][d][rT_pad] fp16 -- the
-  // key tile is rebuilt as W2_K A_K^T in one MFMA chain; for values it
-  // finalizes the split partials.  Value columns are in perm32 order inside
-  // each 32-block (they multiply result tiles), key columns in rank order
-  // (they multiply A_K rows read straight from memory).
-  const _Float16 *W2;
+  // bf16 caches: W2 = B G[h]^T of this layer, [H][d][rT_pad] -- the key
+  // tile is rebuilt as W2_K A_K^T in one MFMA chain (keys: bf16, the dtype
+  // of A_K, rank order); for values it finalizes the split partials (fp16,
+  // columns in perm32 order inside each 32-block, as they multiply result
+  // tiles).
+  const void *W2;
   // Residual codes of this layer.
   // K: [H][T_pad][d*b/8]; a row is 4 chunks (one per 16-lane group g) of
   //    d*b/32 bytes; chunk g holds rotated features i = 32s + 8g + j as slot
@@ -70,6 +70,10 @@ struct CellDev {
   const uint8_t *codes;
   const float *scales;    // this layer: [H][T_pad]
   int32_t rT, rF, bits, rT_pad, rF_pad;
+  // Keys of bf16 caches store A as fp16(A * s) with s a power of two (so
+  // the MFMA key tile reads A_K rows as they are; W2_K holds B G^T / s);
+  // a_inv = 1 / s (1 elsewhere).
+  float a_inv;
 };
 
 struct LayerDev {
@@ -140,6 +144,14 @@ template <typename T>
 __device__ inline gptr<T> gp(const void *p) {
   return (gptr<T>)p;
 }
+// Load at a 32-bit byte offset from a uniform base pointer: compiles to a
+// global load with the base in scalar registers and one 32-bit offset
+// register, with no 64-bit address arithmetic per lane.  Every buffer the
+// kernels read this way is smaller than 4 GiB.
+template <typename T>
+__device__ inline T ldg(const void *base, uint32_t byte_off) {
+  return *(gptr<T>)((const __attribute__((address_space(1))) char *)base + byte_off);
+}
 
 // Copy rows of 16-byte chunks from global memory to LDS with every thread
 // keeping 8 loads in flight (indices are clamped rather than branched on, so
@@ -178,5 +190,6 @@ hipError_t jolt_launch_dense(const jolt::DenseArgs &a, int nseq, hipStream_t s);
 hipError_t jolt_launch_dense_merge(const jolt::DenseArgs &a, int nseq, hipStream_t s);
 hipError_t jolt_launch_unpack(const jolt::LayerDev *layer, int tau, int H, int T, int d,
                               uint8_t *out, hipStream_t s);
-hipError_t jolt_launch_sincos(const float *x, int n, float *sn, float *cs, hipStream_t s);
+hipError_t jolt_launch_sincos(const float *x, int n, float *sn, float *cs, int variant,
+                              hipStream_t s);
 int jolt_mfma_max_lds();

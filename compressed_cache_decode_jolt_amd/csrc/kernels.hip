@@ -35,6 +35,15 @@ __device__ inline float ldf(const void *p, size_t i) {
     return bf16f(((const uint16_t *)p)[i]);
 }
 
+// A_K element: float32 caches as stored; bf16 caches keep A_K as fp16(A * s).
+template <bool F32>
+__device__ inline float ldAk(const CellDev &K, size_t i) {
+  if constexpr (F32)
+    return ((const float *)K.A)[i];
+  else
+    return (float)((const _Float16 *)K.A)[i] * K.a_inv;
+}
+
 __device__ inline float ldq(const void *q, size_t i, bool f32) {
   return f32 ? ((const float *)q)[i] : bf16f(((const uint16_t *)q)[i]);
 }
@@ -120,7 +129,7 @@ __global__ __launch_bounds__(256) void decode_generic(DecodeArgs a) {
       int t = x / K.rF, j = x % K.rF;
       float acc = 0.0f;
       for (int r = 0; r < K.rT; ++r)
-        acc += ldf<F32>(K.A, (size_t)(tt + t) * K.rT_pad + r) *
+        acc += ldAk<F32>(K, (size_t)(tt + t) * K.rT_pad + r) *
                ldf<F32>(K.G, ((size_t)h * K.rF_pad + j) * K.rT_pad + r);
       P[t][j] = acc;
     }
@@ -732,15 +741,21 @@ __global__ void unpack_codes(const LayerDev *layer, int tau, int H, int T, int d
   }
 }
 
-__global__ void sincos_kernel(const float *x, int n, float *sn, float *cs) {
+__global__ void sincos_kernel(const float *x, int n, float *sn, float *cs, int variant) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) fast_sincos(x[i], sn + i, cs + i);
+  if (i < n) {
+    if (variant == 1)
+      hw_sincos(x[i], sn + i, cs + i);
+    else
+      fast_sincos(x[i], sn + i, cs + i);
+  }
 }
 
 }  // namespace
 
-hipError_t jolt_launch_sincos(const float *x, int n, float *sn, float *cs, hipStream_t s) {
-  hipLaunchKernelGGL(sincos_kernel, dim3((n + 255) / 256), dim3(256), 0, s, x, n, sn, cs);
+hipError_t jolt_launch_sincos(const float *x, int n, float *sn, float *cs, int variant,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(sincos_kernel, dim3((n + 255) / 256), dim3(256), 0, s, x, n, sn, cs, variant);
   return hipGetLastError();
 }
 

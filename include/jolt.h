@@ -189,8 +189,12 @@ const char *jolt_last_error(void);
  */
 jolt_status jolt_make_rotation(uint64_t seed, int32_t d, double *out);
 /* jolt_debug_sincos: the kernels' float32 sine and cosine of HOST angles[n]
- *   (evaluated on the current device; synchronous), written to HOST outputs. */
-jolt_status jolt_debug_sincos(const float *angles, int32_t n, float *sin_out, float *cos_out);
+ *   (evaluated on the current device; synchronous), written to HOST outputs.
+ *   variant 0: the polynomial evaluation of the float32 paths and of query
+ *   RoPE; variant 1: the hardware-unit evaluation of the MFMA key path.
+ *   JOLT_E_INVALID for |angle| >= 2^20 or another variant. */
+jolt_status jolt_debug_sincos(const float *angles, int32_t n, float *sin_out, float *cos_out,
+                              int32_t variant);
 jolt_status jolt_debug_unpack(const jolt_cache *cache, int32_t layer, int32_t tau,
                               uint8_t *codes_out, jolt_stream stream);
 

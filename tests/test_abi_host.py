@@ -147,6 +147,7 @@ def test_rope_domain_checked_before_launch():
     # positions above 2^20 or frequencies above 1 are rejected on the host
     assert J.jolt_decode_workspace_size([], 0) == 0
     expect(-1, J.jolt_debug_sincos, np.array([2.0 ** 21], np.float32), match="2\\^20")
+    expect(-1, J.jolt_debug_sincos, np.array([1.0], np.float32), 2, match="variant")
 
 
 def test_long_context_rejected_at_load():
