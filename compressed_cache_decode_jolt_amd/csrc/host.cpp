@@ -202,11 +202,6 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
     for (int r = 0; r < d; ++r)
       for (int c2 = 0; c2 < d; ++c2)
         ((float *)(S.buf.data() + off_pit))[(size_t)c2 * d + r] = (float)Pi64[(size_t)r * d + c2];
-    size_t off_pih = S.take(sizeof(_Float16) * d * d);
-    for (int r = 0; r < d; ++r)
-      for (int c2 = 0; c2 < d; ++c2)
-        ((_Float16 *)(S.buf.data() + off_pih))[(size_t)r * d + c2] =
-            (_Float16)Pi64[(size_t)r * d + (c2 & ~31) + perm32(c2 & 31)];
     size_t off_pik = S.take(sizeof(_Float16) * d * d);
     for (int i = 0; i < d * d; ++i) ((_Float16 *)(S.buf.data() + off_pik))[i] = (_Float16)Pi64[i];
 
@@ -246,8 +241,7 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
         }
         for (int t = 0; t < T; ++t)
           for (int r = 0; r < m.rT; ++r) {
-            size_t dst = tau == 0 ? (size_t)t * m.rT_pad + r
-                                  : (size_t)r * T_pad + (t & ~31) + perm32_inv(t & 31);
+            size_t dst = tau == 0 ? (size_t)t * m.rT_pad + r : av_index(t, r, m.rT_pad);
             if (a16)
               ((_Float16 *)(S.buf.data() + o.A))[dst] =
                   (_Float16)(load_factor(in.A, (size_t)t * m.rT + r, false) * (float)m.a_s);
@@ -293,7 +287,7 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
                 Gf[i] = load_factor(in.G, ((size_t)lp * H + hh) * m.rT * m.rF + i, false);
               for (int f = 0; f < d; ++f)
                 for (int col = 0; col < m.rT_pad; ++col) {
-                  int r = tau == 1 ? (col & ~31) + perm32(col & 31) : col;
+                  const int r = col;
                   double acc = 0.0;
                   if (r < m.rT)
                     for (int j = 0; j < m.rF; ++j) acc += Bf[(size_t)f * m.rF + j] * Gf[(size_t)r * m.rF + j];
@@ -328,9 +322,9 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
                   uint32_t *w = (uint32_t *)(C + ((size_t)h * T_pad + t) * rowb + g2 * (d * b / 32));
                   w[dw] |= code << sh;
                 } else {
-                  code_pos(perm32_inv(t & 31), b, &dw, &sh);
-                  uint32_t *w = (uint32_t *)(C + (((size_t)h * (T_pad / 32) + t / 32) * d + i) * (4 * b));
-                  w[dw] |= code << sh;
+                  size_t at;
+                  vcode_pos(h, t, i, b, T_pad, d, &at, &sh);
+                  *(uint32_t *)(C + at) |= code << sh;
                 }
               }
             }
@@ -354,7 +348,6 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
       std::memset(&L, 0, sizeof L);
       L.Pi = (const float *)(base + off_pi);
       L.PiT = (const float *)(base + off_pit);
-      L.PiH = (const _Float16 *)(base + off_pih);
       L.PiK = (const _Float16 *)(base + off_pik);
       L.T = T;
       L.T_pad = T_pad;
@@ -421,19 +414,22 @@ extern "C" jolt_status jolt_cache_info(const jolt_cache *c, int32_t *n_layers, i
 struct Plan {
   int kernel;        // JOLT_KERNEL_GENERIC or JOLT_KERNEL_MFMA
   int split_tokens, n_split, rV_max, stride, T_max;
-  int lds_bytes;     // MFMA only
-  int nkt;           // MFMA only: max key-rank steps of 32
   size_t ws_bytes;
 };
 
-// The MFMA kernel stages W2_K[h] = B_K G_K[h]^T and (with a key residual)
-// Pi in LDS as fp16 rows padded by 8 elements, next to 8.5 KiB of exchange
-// buffers, 8 KiB of rotated queries and the epilogue's exchange of the value
-// partials; key ranks up to 256 are prefetched a tile ahead in registers and
-// value ranks up to 512 accumulate in registers.
+// The MFMA kernel stages W2_K[h] = B_K G_K[h]^T / s and (with a key
+// residual) Pi in LDS as fp16 rows padded by 8 elements, next to 1 KiB of
+// per-wave softmax state, 8 KiB of rotated queries, the RoPE frequencies,
+// 4 KiB of query MFMA operands and the fp32 sums of the waves' value
+// partials (1 KiB per 16 value ranks, 8 KiB for the residual); after the
+// tile loop the W2_K / Pi region holds every wave's fp16 value partial;
+// key ranks up to 256 are prefetched a tile ahead in registers and value
+// ranks up to 512 accumulate in registers.
 static int mfma_lds_bytes(const CellDev &k, const CellDev &v, int d) {
-  return 2 * d * (k.rT_pad + 8) + (k.bits > 0 ? 2 * d * (d + 8) : 0) + 8704 + 16 * 128 * 4 +
-         512 * (v.rT_pad / 16 + 8);
+  const int kpath = 2 * d * (k.rT_pad + 8) + (k.bits > 0 ? 2 * d * (d + 8) : 0);
+  const int waves = v.rT_pad / 16 > 8 ? 4 : 8;
+  const int park = waves * (v.rT_pad / 16 + 8) * 512;  // fp16 value partials of every wave
+  return std::max(kpath, park) + 1024 + 16 * 128 * 4 + 256 + 4096 + 1024 * (v.rT_pad / 16 + 8);
 }
 
 static bool mfma_ok(const jolt_cache *c, int layer, int *lds) {
@@ -467,25 +463,17 @@ static jolt_status plan_decode(const jolt_cache *const *caches, int batch, int l
   p->T_max = 1;
   p->rV_max = 0;
   bool mf = batch > 0;
-  p->lds_bytes = 0;
-  p->nkt = 0;
   for (int b = 0; b < batch; ++b) {
     const jolt_cache *c = caches[b];
     p->T_max = std::max(p->T_max, c->T);
     p->rV_max = std::max(p->rV_max, c->h_layers[layer].c[1].rT_pad);
     int lds = 0;
     if (!mfma_ok(c, layer, &lds)) mf = false;
-    // one launch runs one (key bits, value bits) instantiation
-    if (c->h_layers[layer].c[0].bits != c0->h_layers[layer].c[0].bits ||
-        c->h_layers[layer].c[1].bits != c0->h_layers[layer].c[1].bits)
-      mf = false;
-    p->lds_bytes = std::max(p->lds_bytes, lds);
-    p->nkt = std::max(p->nkt, c->h_layers[layer].c[0].rT_pad / 32);
   }
   if (want == JOLT_KERNEL_MFMA && !mf)
     return fail(JOLT_E_UNSUPPORTED,
-                "MFMA kernel needs bf16 factors, d=128, key rank <= 256, value rank <= 512, an LDS fit for "
-                "G_K and [B_K|Pi], and the same key/value bits for every sequence");
+                "MFMA kernel needs bf16 factors, d=128, key rank <= 256, value rank <= 512 and an "
+                "LDS fit for W2_K and Pi");
   p->kernel = (want == JOLT_KERNEL_GENERIC || !mf) ? JOLT_KERNEL_GENERIC : JOLT_KERNEL_MFMA;
   const int tile = p->kernel == JOLT_KERNEL_MFMA ? kTokPad : 32;
   int H = batch ? c0->H : 1;
@@ -555,22 +543,50 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
     a.q = (const uint8_t *)q + b0 * qbytes;
     a.out = out + (size_t)b0 * c0->H_q * c0->d;
     a.ws = (float *)workspace + (size_t)b0 * c0->H_q * p.n_split * p.stride;
-    a.nseq = nb;
-    for (int i = 0; i < nb; ++i) {
-      a.seq[i].layer = caches[b0 + i]->d_layers + layer;
-      a.seq[i].q_pos = q_pos[b0 + i];
-      a.seq[i].T = caches[b0 + i]->T;
-    }
     hipError_t e = hipSuccess;
     if (launch && launch->ev_begin && b0 == 0)
       e = hipEventRecord((hipEvent_t)launch->ev_begin, s);
     if (e != hipSuccess) return fail(JOLT_E_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-    e = p.kernel == JOLT_KERNEL_MFMA
-                       ? jolt_launch_mfma(a, nb, caches[b0]->h_layers[layer].c[0].bits,
-                                          caches[b0]->h_layers[layer].c[1].bits, p.nkt,
-                                          p.lds_bytes, s)
-                       : jolt_launch_generic(a, nb, s);
-    if (e != hipSuccess) return fail(JOLT_E_HIP, "split kernel launch: %s", hipGetErrorString(e));
+    if (p.kernel == JOLT_KERNEL_MFMA) {
+      // one launch per (key bits, value bits) class of the chunk's sequences;
+      // every launch writes its sequences' rows of the chunk's workspace
+      bool done[kMaxBatchPerLaunch] = {};
+      for (int i0 = 0; i0 < nb; ++i0) {
+        if (done[i0]) continue;
+        const CellDev &k0 = caches[b0 + i0]->h_layers[layer].c[0];
+        const CellDev &v0 = caches[b0 + i0]->h_layers[layer].c[1];
+        int n = 0, nkt = 0, rv = 0, lds = 0;
+        for (int i = i0; i < nb; ++i) {
+          const jolt_cache *c = caches[b0 + i];
+          const CellDev &k = c->h_layers[layer].c[0], &v = c->h_layers[layer].c[1];
+          if (done[i] || k.bits != k0.bits || v.bits != v0.bits) continue;
+          done[i] = true;
+          a.seq[n].layer = c->d_layers + layer;
+          a.seq[n].q_pos = q_pos[b0 + i];
+          a.seq[n].T = c->T;
+          a.seq[n].slot = i;
+          ++n;
+          nkt = std::max(nkt, k.rT_pad / 32);
+          rv = std::max(rv, v.rT_pad);
+          lds = std::max(lds, mfma_lds_bytes(k, v, c->d));
+        }
+        a.nseq = n;
+        a.rV_max = rv;
+        e = jolt_launch_mfma(a, n, k0.bits, v0.bits, nkt, lds, s);
+        if (e != hipSuccess) return fail(JOLT_E_HIP, "split kernel launch: %s", hipGetErrorString(e));
+      }
+    } else {
+      a.nseq = nb;
+      for (int i = 0; i < nb; ++i) {
+        a.seq[i].layer = caches[b0 + i]->d_layers + layer;
+        a.seq[i].q_pos = q_pos[b0 + i];
+        a.seq[i].T = caches[b0 + i]->T;
+        a.seq[i].slot = i;
+      }
+      e = jolt_launch_generic(a, nb, s);
+      if (e != hipSuccess) return fail(JOLT_E_HIP, "split kernel launch: %s", hipGetErrorString(e));
+    }
+    a.nseq = nb;
     if (launch && launch->ev_end && b0 + nb >= batch)
       e = hipEventRecord((hipEvent_t)launch->ev_end, s);
     if (e != hipSuccess) return fail(JOLT_E_HIP, "hipEventRecord: %s", hipGetErrorString(e));

@@ -20,11 +20,11 @@ constexpr int kMaxBatchPerLaunch = 32;
 constexpr int kMaxD = 128;
 constexpr int kMaxSplits = 2048;
 
-// Token order inside each 32-token block of the value-path layouts: slot
-// q = 8g + j (g = 16-lane group, j = element of the 8-wide operand) holds
-// token perm32(q).  It is the order in which a 16x16 MFMA result tile (lane
-// group g holds rows 4g..4g+3) is re-read as the 32-deep K operand of the next
-// MFMA, so score tiles feed the value products without a transpose.
+// Slot order of a 32-deep MFMA K step built from two 16x16 result tiles:
+// slot q = 8g + j (g = 16-lane group, j = element of the 8-wide operand)
+// holds row perm32(q) of the pair of tiles (lane group g holds rows
+// 4g..4g+3 of each).  The key path feeds its rebuilt feature rows to the
+// score product in this order, and the queries are laid out to match.
 __host__ __device__ inline int perm32(int q) {
   int g = q >> 3, j = q & 7;
   return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
@@ -46,27 +46,49 @@ __host__ __device__ inline void code_pos(int q, int bits, int *dword, int *shift
   *shift = bits * ((P % npair) + (q & 1) * npair);
 }
 
+// Value-side layouts follow the operands of a 16x16x16 MFMA whose K
+// dimension is 16 tokens: lane (row & 15) * 4 + (t & 15) / 4 holds the four
+// consecutive tokens t & ~3 .. (t & ~3) + 3 of one row (a value rank or a
+// rotated feature), so a score tile (lane group g holds tokens 4g..4g+3 of
+// one query) is the other operand as it stands.
+//
+// A_V element (t, r): 16 x 16 tiles per (16-token block, 16-rank block).
+__host__ __device__ inline size_t av_index(int t, int r, int rT_pad) {
+  return (((size_t)(t >> 4) * (rT_pad >> 4) + (r >> 4)) * 64 + (r & 15) * 4 + ((t & 15) >> 2)) * 4 +
+         (t & 3);
+}
+// Value code of (head h, token t, rotated feature f) for b bits and head
+// dim d: per (head, 16-token block) 64 lane records of d*b/32 bytes; the
+// record of lane (f & 15) * 4 + (t & 15) / 4 holds the d/4 slots
+// q = 4 (f / 16) + (t & 3) in code_pos order.  Returns the byte offset of the
+// slot's 32-bit word and the bit offset inside it.
+__host__ __device__ inline void vcode_pos(int h, int t, int f, int bits, int T_pad, int d,
+                                          size_t *byte, int *shift) {
+  int dw, sh;
+  code_pos(4 * (f >> 4) + (t & 3), bits, &dw, &sh);
+  const size_t lane = (size_t)(f & 15) * 4 + ((t & 15) >> 2);
+  *byte = (((size_t)h * (T_pad >> 4) + (t >> 4)) * 64 + lane) * (size_t)(d * bits / 32) + 4 * dw;
+  *shift = sh;
+}
+
 struct CellDev {
   // K: A [T_pad][rT_pad] row-major (fp16, scaled, for bf16 caches).
-  // V: A^T [rT_pad][T_pad], tokens in perm32 order inside 32-token blocks.
+  // V: A in the av_index layout (factor dtype).
   const void *A;
   // K: G^T of this layer, [H][rF_pad][rT_pad].  V: G of this layer,
   // [H][rT_pad][rF_pad].
   const void *G;
   const void *B;          // [d][rF_pad], factor dtype
   const float *Bt;        // V: B^T as float32, [rF_pad][d] (finalize reads)
-  // bf16 caches: W2 = B G[h]^T of this layer, [H][d][rT_pad] -- the key
-  // tile is rebuilt as W2_K A_K^T in one MFMA chain (keys: bf16, the dtype
-  // of A_K, rank order); for values it finalizes the split partials (fp16,
-  // columns in perm32 order inside each 32-block, as they multiply result
-  // tiles).
+  // bf16 caches: W2 = B G[h]^T of this layer, [H][d][rT_pad] fp16 -- the
+  // key tile is rebuilt as W2_K A_K^T in one MFMA chain (keys: divided by
+  // the A_K scale); for values it finalizes the split partials.
   const void *W2;
   // Residual codes of this layer.
   // K: [H][T_pad][d*b/8]; a row is 4 chunks (one per 16-lane group g) of
   //    d*b/32 bytes; chunk g holds rotated features i = 32s + 8g + j as slot
   //    q = 8s + j in code_pos order.
-  // V: [H][T_pad/32][d][4*b]: per (32-token block, feature) the 32 codes of
-  //    slots q = 0..31 (token perm32(q)) in code_pos order.
+  // V: the vcode_pos layout.
   const uint8_t *codes;
   const float *scales;    // this layer: [H][T_pad]
   int32_t rT, rF, bits, rT_pad, rF_pad;
@@ -80,7 +102,6 @@ struct LayerDev {
   CellDev c[2];           // [0] = K, [1] = V
   const float *Pi;        // [d][d] float32, row-major
   const float *PiT;       // Pi^T, [d][d] float32 (finalize reads)
-  const _Float16 *PiH;    // Pi in fp16, [d][d], columns perm32 inside 32-blocks
   const _Float16 *PiK;    // Pi in fp16, [d][d], natural column order
   int32_t T, T_pad, f32;  // f32: factors stored as float32 (else bf16)
 };
@@ -89,6 +110,7 @@ struct SeqArg {
   const LayerDev *layer;  // device pointer to this sequence's layer descriptor
   int32_t q_pos;
   int32_t T;
+  int32_t slot;           // row of this sequence in the launch's q, out and workspace
 };
 
 // Kernel arguments of one split-T launch (passed by value, < 4 KiB).

@@ -59,10 +59,10 @@ __device__ inline int k_code(const CellDev &c, int h, int t, int i, int T_pad, i
 
 __device__ inline int v_code(const CellDev &c, int h, int t, int i, int T_pad, int d) {
   const int b = c.bits;
-  const uint8_t *p = c.codes + (((size_t)h * (T_pad / 32) + t / 32) * d + i) * (4 * b);
-  int dw, sh;
-  code_pos(perm32_inv(t & 31), b, &dw, &sh);
-  uint32_t w = *(const uint32_t *)(p + 4 * dw);
+  size_t at;
+  int sh;
+  vcode_pos(h, t, i, b, T_pad, d, &at, &sh);
+  uint32_t w = *(const uint32_t *)(c.codes + at);
   return (w >> sh) & ((1u << b) - 1u);
 }
 
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256) void decode_generic(DecodeArgs a) {
       float acc = 0.0f;
       for (int t = 0; t < nt; ++t) {
         int tg = tt + t;
-        acc += S[u][t] * ldf<F32>(V.A, (size_t)r * T_pad + (tg & ~31) + perm32_inv(tg & 31));
+        acc += S[u][t] * ldf<F32>(V.A, av_index(tg, r, V.rT_pad));
       }
       float *pa = part0 + u * ustride + 4 + r;
       *pa = al_s[u] * *pa + acc;

@@ -10,11 +10,11 @@ hipError_t launch_bk4(const jolt::DecodeArgs &, int, int, int, int, int, hipStre
 hipError_t launch_bk8(const jolt::DecodeArgs &, int, int, int, int, int, hipStream_t);
 }  // namespace jolt_mfma
 
-// nkt: key-rank steps of 32 (max over the batch); nvb: value-rank 16-row
-// blocks per wave, ceil(rT_pad_V / 64).
+// nkt: key-rank steps of 32, nmv: value-rank blocks of 16 (maxima over the
+// sequences of the launch).
 hipError_t jolt_launch_mfma(const jolt::DecodeArgs &a, int nseq, int bK, int bV, int nkt,
                             int lds_bytes, hipStream_t s) {
-  const int nvb = (a.rV_max / 16 + 3) / 4;
+  const int nvb = a.rV_max / 16;
   switch (bK) {
     case 0: return jolt_mfma::launch_bk0(a, nseq, bV, nkt, nvb, lds_bytes, s);
     case 2: return jolt_mfma::launch_bk2(a, nseq, bV, nkt, nvb, lds_bytes, s);
