@@ -59,11 +59,21 @@ class HipEvents:
             self.hip.hipEventDestroy(C.c_void_p(e))
 
 
-def load_alloc(cfg, ratio):
+def load_alloc(cfg, ratio, seq=0):
+    """(budget key, per-group allocation) of one sequence: the oracle
+    allocator's table for this workload and budget (per sequence where the
+    workload allocates each sequence on its own)."""
     path = os.path.join(ROOT, "tests", "golden", "allocations.json")
     tables = json.load(open(path))[str(cfg.idx)]["tables"]
-    key = ratio if ratio in tables else ("fixed" if "fixed" in tables else sorted(tables)[0])
-    return key, [tuple(map(tuple, g)) for g in tables[key]["groups"]]
+    if "fixed" in tables:
+        key = "fixed"
+    elif f"{ratio}/seq{seq}" in tables:
+        key = f"{ratio}/seq{seq}"
+    elif ratio in tables:
+        key = ratio
+    else:
+        raise SystemExit(f"no allocation for {cfg.name} at {ratio}: have {sorted(tables)}")
+    return key.split("/")[0], [tuple(map(tuple, g)) for g in tables[key]["groups"]]
 
 
 def algorithmic(cfg, alloc, layer):
@@ -130,7 +140,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=1)
-    ap.add_argument("--ratio", default="3x")
+    ap.add_argument("--ratio", default=None, help="byte budget, e.g. 3x (default: the "
+                    "workload's first budget)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "mfma"])
     ap.add_argument("--split-tokens", type=int, default=0, help="tokens per split (0 = auto)")
     ap.add_argument("--dense-split-tokens", type=int, default=0)
@@ -160,15 +171,17 @@ def main():
         return
 
     cfg = get_config(args.config)
-    ratio_key, alloc = load_alloc(cfg, args.ratio)
+    ratio = args.ratio or (f"{cfg.budgets[0]:g}x" if cfg.budgets else "fixed")
+    allocs = [load_alloc(cfg, ratio, s) for s in range(cfg.batch)]
+    ratio_key, alloc = allocs[0]
     kernel = {"auto": None, "generic": J.KERNEL_GENERIC, "mfma": J.KERNEL_MFMA}[args.kernel]
     B, L, H, Hq, d, T = cfg.batch, cfg.n_layers, cfg.H, cfg.H_q, cfg.d, cfg.T
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
     # caches: one synthetic cache per sequence, loaded `copies` times
-    host = [gen.synthetic_cache(cfg, alloc, seq=s) for s in range(B)]
-    step_bytes = B * sum(algorithmic(cfg, alloc, l)[0] for l in range(L))
+    host = [gen.synthetic_cache(cfg, allocs[s][1], seq=s) for s in range(B)]
+    step_bytes = sum(algorithmic(cfg, allocs[s][1], l)[0] for s in range(B) for l in range(L))
     copies = max(1, math.ceil(2 * MALL_BYTES / step_bytes))
     caches = [[J.jolt_load_cache(host[s]) for s in range(B)] for _ in range(copies)]
     inv = gen.rope_inv_freq_input(cfg.rope_base, d)
@@ -208,9 +221,9 @@ def main():
     ev.destroy(evb + eve)
     kern_ms = float(np.mean(split_ms))
 
-    per_launch = [algorithmic(cfg, alloc, l) for l in range(L)]
-    bytes_launch = B * float(np.mean([p[0] for p in per_launch]))
-    flops_launch = B * float(np.mean([p[1] for p in per_launch]))
+    per_launch = [[algorithmic(cfg, allocs[s][1], l) for s in range(B)] for l in range(L)]
+    bytes_launch = float(np.mean([sum(p[0] for p in pl) for pl in per_launch]))
+    flops_launch = float(np.mean([sum(p[1] for p in pl) for pl in per_launch]))
     mfma_bound = flops_launch / PEAK_MFMA_BF16 > bytes_launch / PEAK_HBM
     kname = ("decode_mfma" if args.kernel != "generic" and cfg.factor_dtype == "bf16" and d == 128
              else "decode_generic")

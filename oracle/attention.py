@@ -33,25 +33,29 @@ def group_of(cache, layer):
     raise IndexError(layer)
 
 
-def residual(cell, lp, d):
-    """deq(codes) in the rotated basis for layer index lp: [H, T, d] or None."""
+def residual(cell, lp, d, heads=None):
+    """deq(codes) in the rotated basis for layer index lp: [H, T, d] (or the
+    listed heads only) or None."""
     if cell["bits"] == 0:
         return None
-    codes = unpack(cell["codes"][lp], cell["bits"], d)
-    return dequantize(codes, cell["scales"][lp], cell["bits"])
+    hs = slice(None) if heads is None else list(heads)
+    codes = unpack(cell["codes"][lp][hs], cell["bits"], d)
+    return dequantize(codes, cell["scales"][lp][hs], cell["bits"])
 
 
-def decode_cell(cell, lp, d, Pi):
-    """X^[lp] of one stored cell: [H, T, d] float64."""
+def decode_cell(cell, lp, d, Pi, heads=None):
+    """X^[lp] of one stored cell: [H, T, d] float64 (or [len(heads), T, d]
+    for the listed heads; large workloads decode a sample of heads)."""
+    hs = slice(None) if heads is None else list(heads)
     A = cell["A"].astype(np.float64)
     B = cell["B"].astype(np.float64)
-    G = cell["G"][lp].astype(np.float64)
+    G = cell["G"][lp][hs].astype(np.float64)
     H = G.shape[0]
     T = A.shape[0]
     out = np.zeros((H, T, d))
     if cell["r_T"] > 0:
         out += np.einsum("tr,hrs,fs->htf", A, G, B, optimize=True)
-    R = residual(cell, lp, d)
+    R = residual(cell, lp, d, heads)
     if R is not None:
         out += R @ Pi.T
     return out
@@ -79,11 +83,12 @@ def decode_layer(cache, layer, q, q_pos, inv_freq, scale, Pi=None, heads=None):
     qr = rope(np.asarray(q, dtype=np.float64), q_pos, inv_freq)
     pos = np.arange(T)
     out = np.full((H_q, d), np.nan)
-    Khat = decode_cell(cK, lp, d, Pi)
-    Vhat = decode_cell(cV, lp, d, Pi)
-    for h in heads:
-        Kr = rope(Khat[h], pos, inv_freq)
-        out[h * Hg:(h + 1) * Hg] = softmax_attention(qr[h * Hg:(h + 1) * Hg], Kr, Vhat[h], scale)
+    heads = list(heads)
+    Khat = decode_cell(cK, lp, d, Pi, heads)
+    Vhat = decode_cell(cV, lp, d, Pi, heads)
+    for n, h in enumerate(heads):
+        Kr = rope(Khat[n], pos, inv_freq)
+        out[h * Hg:(h + 1) * Hg] = softmax_attention(qr[h * Hg:(h + 1) * Hg], Kr, Vhat[n], scale)
     return out
 
 

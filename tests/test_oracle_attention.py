@@ -127,6 +127,18 @@ def test_q_zero_gives_mean_and_T1_gives_first():
         assert np.allclose(o1[j], V[j // 2, 0], atol=1e-13)
 
 
+def test_head_subset_matches_full_decode():
+    """Decoding a sample of KV heads gives exactly those rows of the full
+    decode (the large GPU parity cases sample heads this way)."""
+    cache = gen.small_cache(11, 50, 4, 8, 16, [((8, 8, 4), (8, 8, 2))], [2], factor_dtype="f32")
+    inv = gen.rope_inv_freq_input(1e4, 16)
+    q = np.random.default_rng(3).standard_normal((8, 16))
+    full = att.decode_layer(cache, 1, q, 50, inv, 0.25)
+    sub = att.decode_layer(cache, 1, q, 50, inv, 0.25, heads=[3, 1])
+    assert np.array_equal(sub[2:4], full[2:4]) and np.array_equal(sub[6:8], full[6:8])
+    assert np.isnan(sub[0:2]).all() and np.isnan(sub[4:6]).all()
+
+
 def test_gqa_equals_mha_head_by_head():
     cache, _ = tiny_cache(H_q=2)          # one query per KV head
     inv = gen.rope_inv_freq_input(1e4, 8)
