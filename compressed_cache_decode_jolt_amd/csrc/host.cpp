@@ -202,8 +202,12 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
     for (int r = 0; r < d; ++r)
       for (int c2 = 0; c2 < d; ++c2)
         ((float *)(S.buf.data() + off_pit))[(size_t)c2 * d + r] = (float)Pi64[(size_t)r * d + c2];
-    size_t off_pik = S.take(sizeof(_Float16) * d * d);
-    for (int i = 0; i < d * d; ++i) ((_Float16 *)(S.buf.data() + off_pik))[i] = (_Float16)Pi64[i];
+    // Pi in fp16 with padded rows: the MFMA kernel copies it to LDS as it is
+    const int pik_row = d + kRowPad;
+    size_t off_pik = S.take(sizeof(_Float16) * d * pik_row);
+    for (int r = 0; r < d; ++r)
+      for (int c2 = 0; c2 < d; ++c2)
+        ((_Float16 *)(S.buf.data() + off_pik))[(size_t)r * pik_row + c2] = (_Float16)Pi64[(size_t)r * d + c2];
 
     struct Offs {
       size_t A, B, Bt;
@@ -277,7 +281,9 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
           // a_s, the scale of the fp16 A_K) and value-finalize matrix, fp16,
           // formed in float64 and rounded once
           if (!f32 && m.rT > 0) {
-            size_t ow = S.take(sizeof(uint16_t) * H * d * m.rT_pad);
+            // key rows padded like their LDS image
+            const int w2_row = m.rT_pad + (tau == 0 ? kRowPad : 0);
+            size_t ow = S.take(sizeof(uint16_t) * H * d * w2_row);
             o.W2.push_back(ow);
             _Float16 *W2 = (_Float16 *)(S.buf.data() + ow);
             std::vector<double> Bf((size_t)d * m.rF), Gf((size_t)m.rT * m.rF);
@@ -291,7 +297,7 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
                   double acc = 0.0;
                   if (r < m.rT)
                     for (int j = 0; j < m.rF; ++j) acc += Bf[(size_t)f * m.rF + j] * Gf[(size_t)r * m.rF + j];
-                  W2[((size_t)hh * d + f) * m.rT_pad + col] = (_Float16)(acc / m.a_s);
+                  W2[((size_t)hh * d + f) * w2_row + col] = (_Float16)(acc / m.a_s);
                 }
             }
           } else {
@@ -441,6 +447,20 @@ static bool mfma_ok(const jolt_cache *c, int layer, int *lds) {
   return *lds <= jolt_mfma_max_lds();
 }
 
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 static jolt_status plan_decode(const jolt_cache *const *caches, int batch, int layer,
                                const jolt_launch *launch, Plan *p) {
   if (batch < 0) return fail(JOLT_E_INVALID, "batch=%d", batch);
@@ -479,7 +499,10 @@ static jolt_status plan_decode(const jolt_cache *const *caches, int batch, int l
   int H = batch ? c0->H : 1;
   int split = launch && launch->split_tokens > 0 ? launch->split_tokens : 0;
   if (split == 0) {
-    int want_wg = 512;
+    // one workgroup per compute unit: the MFMA kernel holds a CU alone
+    // (LDS and registers), and fewer, longer splits pay the per-workgroup
+    // prologue and epilogue less often
+    int want_wg = p->kernel == JOLT_KERNEL_MFMA ? cu_count() : 512;
     int n = std::max(1, (want_wg + batch * H - 1) / std::max(1, batch * H));
     split = (p->T_max + n - 1) / n;
   }
@@ -548,8 +571,9 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
       e = hipEventRecord((hipEvent_t)launch->ev_begin, s);
     if (e != hipSuccess) return fail(JOLT_E_HIP, "hipEventRecord: %s", hipGetErrorString(e));
     if (p.kernel == JOLT_KERNEL_MFMA) {
-      // one launch per (key bits, value bits) class of the chunk's sequences;
-      // every launch writes its sequences' rows of the chunk's workspace
+      // one launch per (key bits, value bits, key-rank steps) class of the
+      // chunk's sequences; every launch writes its sequences' rows of the
+      // chunk's workspace
       bool done[kMaxBatchPerLaunch] = {};
       for (int i0 = 0; i0 < nb; ++i0) {
         if (done[i0]) continue;
@@ -559,14 +583,14 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
         for (int i = i0; i < nb; ++i) {
           const jolt_cache *c = caches[b0 + i];
           const CellDev &k = c->h_layers[layer].c[0], &v = c->h_layers[layer].c[1];
-          if (done[i] || k.bits != k0.bits || v.bits != v0.bits) continue;
+          if (done[i] || k.bits != k0.bits || v.bits != v0.bits || k.rT_pad != k0.rT_pad) continue;
           done[i] = true;
           a.seq[n].layer = c->d_layers + layer;
           a.seq[n].q_pos = q_pos[b0 + i];
           a.seq[n].T = c->T;
           a.seq[n].slot = i;
           ++n;
-          nkt = std::max(nkt, k.rT_pad / 32);
+          nkt = k.rT_pad / kRankPad;
           rv = std::max(rv, v.rT_pad);
           lds = std::max(lds, mfma_lds_bytes(k, v, c->d));
         }

@@ -15,6 +15,8 @@ namespace jolt {
 
 constexpr int kTokPad = 128;    // T padding: one MFMA workgroup tile
 constexpr int kRankPad = 32;    // rank padding: one 16x16x32 MFMA K-step
+constexpr int kRowPad = 8;      // fp16 elements appended to each row of the key-tile
+                                // matrices (W2_K, Pi), which are copied to LDS as they are
 constexpr int kMaxHg = 16;      // query heads per KV head
 constexpr int kMaxBatchPerLaunch = 32;
 constexpr int kMaxD = 128;
@@ -80,9 +82,10 @@ struct CellDev {
   const void *G;
   const void *B;          // [d][rF_pad], factor dtype
   const float *Bt;        // V: B^T as float32, [rF_pad][d] (finalize reads)
-  // bf16 caches: W2 = B G[h]^T of this layer, [H][d][rT_pad] fp16 -- the
-  // key tile is rebuilt as W2_K A_K^T in one MFMA chain (keys: divided by
-  // the A_K scale); for values it finalizes the split partials.
+  // bf16 caches: W2 = B G[h]^T of this layer, fp16 -- the key tile is
+  // rebuilt as W2_K A_K^T in one MFMA chain (keys: [H][d][rT_pad + kRowPad],
+  // divided by the A_K scale); for values ([H][d][rT_pad]) it finalizes the
+  // split partials.
   const void *W2;
   // Residual codes of this layer.
   // K: [H][T_pad][d*b/8]; a row is 4 chunks (one per 16-lane group g) of
@@ -102,7 +105,7 @@ struct LayerDev {
   CellDev c[2];           // [0] = K, [1] = V
   const float *Pi;        // [d][d] float32, row-major
   const float *PiT;       // Pi^T, [d][d] float32 (finalize reads)
-  const _Float16 *PiK;    // Pi in fp16, [d][d], natural column order
+  const _Float16 *PiK;    // Pi in fp16, [d][d + kRowPad] (padded rows)
   int32_t T, T_pad, f32;  // f32: factors stored as float32 (else bf16)
 };
 

@@ -4,23 +4,37 @@
 #include "jolt_internal.h"
 
 namespace jolt_mfma {
-hipError_t launch_bk0(const jolt::DecodeArgs &, int, int, int, int, int, hipStream_t);
-hipError_t launch_bk2(const jolt::DecodeArgs &, int, int, int, int, int, hipStream_t);
-hipError_t launch_bk4(const jolt::DecodeArgs &, int, int, int, int, int, hipStream_t);
-hipError_t launch_bk8(const jolt::DecodeArgs &, int, int, int, int, int, hipStream_t);
+hipError_t launch_k0_v0(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k0_v2(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k0_v4(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k0_v8(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k2_v0(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k2_v2(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k2_v4(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k2_v8(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k4_v0(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k4_v2(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k4_v4(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k4_v8(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k8_v0(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k8_v2(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k8_v4(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k8_v8(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
 }  // namespace jolt_mfma
 
-// nkt: key-rank steps of 32, nmv: value-rank blocks of 16 (maxima over the
-// sequences of the launch).
+// nkt: key-rank steps of 32 (the same for every sequence of the launch);
+// the value-rank blocks of 16 are the launch's maximum.
 hipError_t jolt_launch_mfma(const jolt::DecodeArgs &a, int nseq, int bK, int bV, int nkt,
                             int lds_bytes, hipStream_t s) {
-  const int nvb = a.rV_max / 16;
-  switch (bK) {
-    case 0: return jolt_mfma::launch_bk0(a, nseq, bV, nkt, nvb, lds_bytes, s);
-    case 2: return jolt_mfma::launch_bk2(a, nseq, bV, nkt, nvb, lds_bytes, s);
-    case 4: return jolt_mfma::launch_bk4(a, nseq, bV, nkt, nvb, lds_bytes, s);
-    default: return jolt_mfma::launch_bk8(a, nseq, bV, nkt, nvb, lds_bytes, s);
-  }
+  using namespace jolt_mfma;
+  typedef hipError_t (*fn)(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
+  static const fn table[4][4] = {
+      {launch_k0_v0, launch_k0_v2, launch_k0_v4, launch_k0_v8},
+      {launch_k2_v0, launch_k2_v2, launch_k2_v4, launch_k2_v8},
+      {launch_k4_v0, launch_k4_v2, launch_k4_v4, launch_k4_v8},
+      {launch_k8_v0, launch_k8_v2, launch_k8_v4, launch_k8_v8}};
+  auto idx = [](int b) { return b == 0 ? 0 : b == 2 ? 1 : b == 4 ? 2 : 3; };
+  return table[idx(bK)][idx(bV)](a, nseq, nkt, a.rV_max / 16, lds_bytes, s);
 }
 
 // LDS available to one workgroup on gfx950 (160 KiB per CU).

@@ -1,0 +1,46 @@
+// Instantiations of the MFMA decode kernel for 4-bit key and 4-bit value residuals.
+#include "decode_mfma.inc"
+
+namespace jolt_mfma {
+
+template <int KT, int MV, int WAVES>
+static hipError_t go(const jolt::DecodeArgs &a, int nseq, int lds, hipStream_t s) {
+  auto k = decode_mfma<4, 4, KT, MV, WAVES>;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       160 * 1024);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  dim3 grid((unsigned)(nseq * a.n_split * a.H));
+  hipLaunchKernelGGL(k, grid, dim3(64 * WAVES), lds, s, a);
+  return hipGetLastError();
+}
+
+// value classes: ranks <= 64 or <= 128 with 8 waves (two per SIMD), <= 512
+// with 4 waves holding the accumulators of 32 rank blocks each
+template <int KT>
+static hipError_t go_kt(const jolt::DecodeArgs &a, int nseq, int nmv, int lds, hipStream_t s) {
+  if (nmv > 8) return go<KT, 32, 4>(a, nseq, lds, s);
+  if (nmv > 4) return go<KT, 8, 8>(a, nseq, lds, s);
+  return go<KT, 4, 8>(a, nseq, lds, s);
+}
+
+// nkt: exact key-rank steps of 32 (0..8)
+hipError_t launch_k4_v4(const jolt::DecodeArgs &a, int nseq, int nkt, int nmv, int lds,
+                          hipStream_t s) {
+  switch (nkt) {
+    case 0: return go_kt<0>(a, nseq, nmv, lds, s);
+    case 1: return go_kt<1>(a, nseq, nmv, lds, s);
+    case 2: return go_kt<2>(a, nseq, nmv, lds, s);
+    case 3: return go_kt<3>(a, nseq, nmv, lds, s);
+    case 4: return go_kt<4>(a, nseq, nmv, lds, s);
+    case 5: return go_kt<5>(a, nseq, nmv, lds, s);
+    case 6: return go_kt<6>(a, nseq, nmv, lds, s);
+    case 7: return go_kt<7>(a, nseq, nmv, lds, s);
+    default: return go_kt<8>(a, nseq, nmv, lds, s);
+  }
+}
+
+}  // namespace jolt_mfma
