@@ -8,9 +8,13 @@ compressed caches already resident in HBM.  The default workload is one
 Llama-3.1-8B-shaped layer (8 KV / 32 query heads, d=128, T=4096, batch 1)
 compressed at the allocator's 3x budget.  Small caches are rotated over enough
 device copies (> 512 MiB) that a step reads HBM, not the 256 MiB Infinity
-Cache.  Prints one JSON line: compressed-context tokens/s, the dominant
-kernel's roofline position (timed live with HIP events around that kernel),
-the dense decode comparator on the same shape and the CPU oracle baseline.
+Cache.  The timed steps run twice: eagerly, with HIP events recorded by the
+library around each split-kernel launch on its stream (the kernel time of the
+roofline figure), and captured once into a HIP graph that is replayed (the
+step time reported as `value`; --no-graph reports the eager time instead).
+Prints one JSON line: compressed-context tokens/s, the dominant kernel's
+roofline position, the dense decode comparator on the same shape (timed the
+same way) and the CPU oracle baseline.
 """
 import argparse
 import ctypes as C
@@ -148,6 +152,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (default: the timed steps are also captured "
+                         "in one HIP graph and replayed; value comes from the replay)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -202,24 +209,58 @@ def main():
 
     def step(i, timed):
         cs = caches[i % copies]
+        st = torch.cuda.current_stream()
         for l in range(L):
             e = (evb[(i * L + l) % n_ev], eve[(i * L + l) % n_ev]) if timed else None
             J.jolt_decode_attention(cs, l, qs[l], q_pos, inv, scale, out, ws, kernel=kernel,
-                                    split_tokens=split, stream=stream, events=e)
+                                    split_tokens=split, stream=st, events=e)
 
-    for i in range(args.warmup):
-        step(i, False)
-    torch.cuda.synchronize()
-    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_start.record()
-    for i in range(args.steps):
-        step(i, True)
-    t_stop.record()
-    torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_stop) / args.steps
+    def timed_steps(run):
+        """Warm-up steps, then exactly args.steps steps between two events."""
+        for i in range(args.warmup):
+            run(i, False)
+        torch.cuda.synchronize()
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        run(None, True)
+        b_.record()
+        torch.cuda.synchronize()
+        return a_.elapsed_time(b_) / args.steps
+
+    # eager: every launch bracketed by HIP events on its stream (kernel time)
+    def eager(i, timed):
+        if i is not None:
+            step(i, timed)
+        else:
+            for k in range(args.steps):
+                step(k, True)
+    eager_ms = timed_steps(eager)
     split_ms = [ev.elapsed_ms(a, b) for a, b in zip(evb, eve)]
     ev.destroy(evb + eve)
     kern_ms = float(np.mean(split_ms))
+
+    def graphed(run_step, n):
+        """One HIP graph holding n steps (copies rotate as in eager mode)."""
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run_step(0, False)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for k in range(n):
+                run_step(k, False)
+        torch.cuda.synchronize()
+        return g
+
+    ms_per_step = eager_ms
+    graph_ms = None
+    if not args.no_graph:
+        g = graphed(step, args.steps)
+        graph_ms = timed_steps(lambda i, t: g.replay() if i is None else step(i, False))
+        ms_per_step = graph_ms
+        del g
 
     per_launch = [[algorithmic(cfg, allocs[s][1], l) for s in range(B)] for l in range(L)]
     bytes_launch = float(np.mean([sum(p[0] for p in pl) for pl in per_launch]))
@@ -253,23 +294,24 @@ def main():
         dws = torch.zeros(J.jolt_dense_workspace_size(B, H, Hq, d, T, split_tokens=dsplit),
                           dtype=torch.uint8, device=dev)
 
-        def dstep(i):
+        def dstep(i, timed=False):
+            st = torch.cuda.current_stream()
             for l in range(L):
                 k, v = kv[i % dcopies][l]
                 J.jolt_dense_attention(k, v, qs[l], q_pos, inv, scale, out, dws,
-                                       split_tokens=dsplit, stream=stream)
+                                       split_tokens=dsplit, stream=st)
 
-        for i in range(args.warmup):
-            dstep(i)
-        torch.cuda.synchronize()
-        t_start.record()
-        for i in range(args.steps):
-            dstep(i)
-        t_stop.record()
-        torch.cuda.synchronize()
-        dms = t_start.elapsed_time(t_stop) / args.steps
-        dense = {"ms_per_step": dms, "hbm_GBps": dense_step / (dms * 1e-3) / 1e9,
-                 "jolt_speedup": dms / ms_per_step}
+        d_eager = timed_steps(lambda i, t: [dstep(k) for k in range(args.steps)]
+                              if i is None else dstep(i))
+        dms = d_eager
+        d_graph = None
+        if not args.no_graph:
+            dg = graphed(dstep, args.steps)
+            d_graph = timed_steps(lambda i, t: dg.replay() if i is None else dstep(i))
+            dms = d_graph
+            del dg
+        dense = {"ms_per_step": dms, "eager_ms_per_step": d_eager, "graph_ms_per_step": d_graph,
+                 "hbm_GBps": dense_step / (dms * 1e-3) / 1e9, "jolt_speedup": dms / ms_per_step}
         del kv
 
     cpu = None if args.no_cpu else cpu_baseline(cfg, host[0], args.cpu_seconds)
@@ -284,6 +326,8 @@ def main():
                    "allocation": [list(map(list, a)) for a in alloc[:1]] if L == 1 else ratio_key,
                    "kernel": args.kernel, "split_tokens": split, "cache_copies": copies,
                    "step_alg_bytes": step_bytes},
+        "timing": {"eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
+                   "reported": "graph" if graph_ms is not None else "eager"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "dense": dense,

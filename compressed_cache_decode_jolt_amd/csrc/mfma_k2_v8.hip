@@ -3,9 +3,9 @@
 
 namespace jolt_mfma {
 
-template <int KT, int MV, int WAVES>
+template <int KT, int MV, int WAVES, int NB>
 static hipError_t go(const jolt::DecodeArgs &a, int nseq, int lds, hipStream_t s) {
-  auto k = decode_mfma<2, 8, KT, MV, WAVES>;
+  auto k = decode_mfma<2, 8, KT, MV, WAVES, NB>;
   static bool attr = false;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -22,9 +22,9 @@ static hipError_t go(const jolt::DecodeArgs &a, int nseq, int lds, hipStream_t s
 // with 4 waves holding the accumulators of 32 rank blocks each
 template <int KT>
 static hipError_t go_kt(const jolt::DecodeArgs &a, int nseq, int nmv, int lds, hipStream_t s) {
-  if (nmv > 8) return go<KT, 32, 4>(a, nseq, lds, s);
-  if (nmv > 4) return go<KT, 8, 8>(a, nseq, lds, s);
-  return go<KT, 4, 8>(a, nseq, lds, s);
+  if (nmv > 8) return go<KT, 32, 4, 1>(a, nseq, lds, s);
+  if (nmv > 4) return go<KT, 8, 8, 1>(a, nseq, lds, s);
+  return go<KT, 4, 8, 1>(a, nseq, lds, s);
 }
 
 // nkt: exact key-rank steps of 32 (0..8)
