@@ -435,7 +435,9 @@ static int mfma_lds_bytes(const CellDev &k, const CellDev &v, int d) {
   const int kpath = 2 * d * (k.rT_pad + 8) + (k.bits > 0 ? 2 * d * (d + 8) : 0);
   const int waves = v.rT_pad / 16 > 8 ? 4 : 8;
   const int park = waves * (v.rT_pad / 16 + 8) * 512;  // fp16 value partials of every wave
-  return std::max(kpath, park) + 1024 + 16 * 128 * 4 + 256 + 4096 + 1024 * (v.rT_pad / 16 + 8);
+  // + softmax reduction, query staging, frequencies, query operands, combined
+  // value tiles and the token-block counter
+  return std::max(kpath, park) + 1024 + 16 * 128 * 4 + 256 + 4096 + 1024 * (v.rT_pad / 16 + 8) + 16;
 }
 
 static bool mfma_ok(const jolt_cache *c, int layer, int *lds) {
@@ -574,6 +576,19 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
       // one launch per (key bits, value bits, key-rank steps) class of the
       // chunk's sequences; every launch writes its sequences' rows of the
       // chunk's workspace
+      MfmaArgs ma;
+      std::memset(&ma, 0, sizeof ma);
+      ma.q = a.q;
+      ma.ws = a.ws;
+      std::memcpy(ma.inv_freq, a.inv_freq, sizeof ma.inv_freq);
+      ma.scale = a.scale;
+      ma.q_f32 = a.q_f32;
+      ma.H = a.H;
+      ma.H_q = a.H_q;
+      ma.Hg = a.Hg;
+      ma.n_split = a.n_split;
+      ma.split_tokens = a.split_tokens;
+      ma.stride = a.stride;
       bool done[kMaxBatchPerLaunch] = {};
       for (int i0 = 0; i0 < nb; ++i0) {
         if (done[i0]) continue;
@@ -585,18 +600,30 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
           const CellDev &k = c->h_layers[layer].c[0], &v = c->h_layers[layer].c[1];
           if (done[i] || k.bits != k0.bits || v.bits != v0.bits || k.rT_pad != k0.rT_pad) continue;
           done[i] = true;
-          a.seq[n].layer = c->d_layers + layer;
-          a.seq[n].q_pos = q_pos[b0 + i];
-          a.seq[n].T = c->T;
-          a.seq[n].slot = i;
+          const LayerDev &L = c->h_layers[layer];
+          SeqMfma &m = ma.seq[n];
+          m.kA = k.A;
+          m.kcodes = k.codes;
+          m.kW2 = k.W2;
+          m.kscales = k.scales;
+          m.vA = v.A;
+          m.vcodes = v.codes;
+          m.vW2 = v.W2;
+          m.vscales = v.scales;
+          m.PiK = L.PiK;
+          m.T = c->T;
+          m.T_pad = L.T_pad;
+          m.q_pos = q_pos[b0 + i];
+          m.slot = i;
+          m.vrT_pad = v.rT_pad;
           ++n;
           nkt = k.rT_pad / kRankPad;
           rv = std::max(rv, v.rT_pad);
           lds = std::max(lds, mfma_lds_bytes(k, v, c->d));
         }
-        a.nseq = n;
-        a.rV_max = rv;
-        e = jolt_launch_mfma(a, n, k0.bits, v0.bits, nkt, lds, s);
+        ma.nseq = n;
+        ma.rV_max = rv;
+        e = jolt_launch_mfma(ma, n, k0.bits, v0.bits, nkt, lds, s);
         if (e != hipSuccess) return fail(JOLT_E_HIP, "split kernel launch: %s", hipGetErrorString(e));
       }
     } else {

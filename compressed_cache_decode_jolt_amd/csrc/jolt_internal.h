@@ -130,6 +130,30 @@ struct DecodeArgs {
   SeqArg seq[kMaxBatchPerLaunch];
 };
 
+// What the MFMA kernel reads of one sequence's layer: the fields of its
+// descriptor copied into the kernel arguments, so that a workgroup's first
+// data loads do not wait on a descriptor load.
+struct SeqMfma {
+  const void *kA, *kcodes, *kW2;
+  const float *kscales;
+  const void *vA, *vcodes, *vW2;
+  const float *vscales;
+  const _Float16 *PiK;
+  int32_t T, T_pad, q_pos, slot, vrT_pad, pad_;
+};
+
+// Kernel arguments of one MFMA split-T launch (passed by value).
+struct MfmaArgs {
+  const void *q;          // [batch][H_q][d]
+  float *ws;              // partials [batch][H_q][n_split][stride]
+  float inv_freq[kMaxD / 2];
+  float scale;
+  int32_t q_f32, H, H_q, Hg;
+  int32_t n_split, split_tokens, stride, rV_max, nseq;
+  SeqMfma seq[kMaxBatchPerLaunch];
+};
+static_assert(sizeof(MfmaArgs) <= 4096, "MFMA kernel arguments exceed 4 KiB");
+
 // A generic-kernel partial is [m, l, 0, 0, a[rV_max], c[d]] (floats); an
 // MFMA-kernel or dense partial is [m, l, 0, 0, o[d]] with o already
 // projected to output space and divided by l; m = -inf, l = 0 for an empty
@@ -207,7 +231,7 @@ __device__ inline void stage_rows(uint8_t *dst, int dst_stride, const void *src,
 
 // Kernel launchers (kernels_*.hip).  Each returns the hipError_t of its launch.
 hipError_t jolt_launch_generic(const jolt::DecodeArgs &a, int nseq, hipStream_t s);
-hipError_t jolt_launch_mfma(const jolt::DecodeArgs &a, int nseq, int bK, int bV, int nkt,
+hipError_t jolt_launch_mfma(const jolt::MfmaArgs &a, int nseq, int bK, int bV, int nkt,
                             int lds_bytes, hipStream_t s);
 hipError_t jolt_launch_merge(const jolt::DecodeArgs &a, int nseq, hipStream_t s);
 hipError_t jolt_launch_merge_outputs(const jolt::DecodeArgs &a, int nseq, hipStream_t s);

@@ -4,30 +4,30 @@
 #include "jolt_internal.h"
 
 namespace jolt_mfma {
-hipError_t launch_k0_v0(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
-hipError_t launch_k0_v2(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
-hipError_t launch_k0_v4(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
-hipError_t launch_k0_v8(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
-hipError_t launch_k2_v0(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
-hipError_t launch_k2_v2(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
-hipError_t launch_k2_v4(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
-hipError_t launch_k2_v8(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
-hipError_t launch_k4_v0(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
-hipError_t launch_k4_v2(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
-hipError_t launch_k4_v4(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
-hipError_t launch_k4_v8(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
-hipError_t launch_k8_v0(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
-hipError_t launch_k8_v2(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
-hipError_t launch_k8_v4(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
-hipError_t launch_k8_v8(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k0_v0(const jolt::MfmaArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k0_v2(const jolt::MfmaArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k0_v4(const jolt::MfmaArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k0_v8(const jolt::MfmaArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k2_v0(const jolt::MfmaArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k2_v2(const jolt::MfmaArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k2_v4(const jolt::MfmaArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k2_v8(const jolt::MfmaArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k4_v0(const jolt::MfmaArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k4_v2(const jolt::MfmaArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k4_v4(const jolt::MfmaArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k4_v8(const jolt::MfmaArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k8_v0(const jolt::MfmaArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k8_v2(const jolt::MfmaArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k8_v4(const jolt::MfmaArgs &, int, int, int, int, hipStream_t);
+hipError_t launch_k8_v8(const jolt::MfmaArgs &, int, int, int, int, hipStream_t);
 }  // namespace jolt_mfma
 
 // nkt: key-rank steps of 32 (the same for every sequence of the launch);
 // the value-rank blocks of 16 are the launch's maximum.
-hipError_t jolt_launch_mfma(const jolt::DecodeArgs &a, int nseq, int bK, int bV, int nkt,
+hipError_t jolt_launch_mfma(const jolt::MfmaArgs &a, int nseq, int bK, int bV, int nkt,
                             int lds_bytes, hipStream_t s) {
   using namespace jolt_mfma;
-  typedef hipError_t (*fn)(const jolt::DecodeArgs &, int, int, int, int, hipStream_t);
+  typedef hipError_t (*fn)(const jolt::MfmaArgs &, int, int, int, int, hipStream_t);
   static const fn table[4][4] = {
       {launch_k0_v0, launch_k0_v2, launch_k0_v4, launch_k0_v8},
       {launch_k2_v0, launch_k2_v2, launch_k2_v4, launch_k2_v8},

@@ -4,7 +4,7 @@
 namespace jolt_mfma {
 
 template <int KT, int MV, int WAVES, int NB>
-static hipError_t go(const jolt::DecodeArgs &a, int nseq, int lds, hipStream_t s) {
+static hipError_t go(const jolt::MfmaArgs &a, int nseq, int lds, hipStream_t s) {
   auto k = decode_mfma<8, 2, KT, MV, WAVES, NB>;
   static bool attr = false;
   if (!attr) {
@@ -21,14 +21,14 @@ static hipError_t go(const jolt::DecodeArgs &a, int nseq, int lds, hipStream_t s
 // value classes: ranks <= 64 or <= 128 with 8 waves (two per SIMD), <= 512
 // with 4 waves holding the accumulators of 32 rank blocks each
 template <int KT>
-static hipError_t go_kt(const jolt::DecodeArgs &a, int nseq, int nmv, int lds, hipStream_t s) {
+static hipError_t go_kt(const jolt::MfmaArgs &a, int nseq, int nmv, int lds, hipStream_t s) {
   if (nmv > 8) return go<KT, 32, 4, 1>(a, nseq, lds, s);
   if (nmv > 4) return go<KT, 8, 8, 1>(a, nseq, lds, s);
   return go<KT, 4, 8, 1>(a, nseq, lds, s);
 }
 
 // nkt: exact key-rank steps of 32 (0..8)
-hipError_t launch_k8_v2(const jolt::DecodeArgs &a, int nseq, int nkt, int nmv, int lds,
+hipError_t launch_k8_v2(const jolt::MfmaArgs &a, int nseq, int nkt, int nmv, int lds,
                           hipStream_t s) {
   switch (nkt) {
     case 0: return go_kt<0>(a, nseq, nmv, lds, s);
