@@ -435,9 +435,9 @@ static int mfma_lds_bytes(const CellDev &k, const CellDev &v, int d) {
   const int kpath = 2 * d * (k.rT_pad + 8) + (k.bits > 0 ? 2 * d * (d + 8) : 0);
   const int waves = v.rT_pad / 16 > 8 ? 4 : 8;
   const int park = waves * (v.rT_pad / 16 + 8) * 512;  // fp16 value partials of every wave
-  // + softmax reduction, query staging, frequencies, query operands, combined
-  // value tiles and the token-block counter
-  return std::max(kpath, park) + 1024 + 16 * 128 * 4 + 256 + 4096 + 1024 * (v.rT_pad / 16 + 8) + 16;
+  // + softmax reduction, frequencies, query operands, combined value tiles
+  // and the token-block counter
+  return std::max(kpath, park) + 1024 + 256 + 4096 + 1024 * (v.rT_pad / 16 + 8) + 16;
 }
 
 static bool mfma_ok(const jolt_cache *c, int layer, int *lds) {

@@ -13,7 +13,7 @@ static hipError_t go(const jolt::MfmaArgs &a, int nseq, int lds, hipStream_t s) 
     if (e != hipSuccess) return e;
     attr = true;
   }
-  dim3 grid((unsigned)(nseq * a.n_split * a.H));
+  dim3 grid((unsigned)(a.n_split * a.H), (unsigned)nseq);
   hipLaunchKernelGGL(k, grid, dim3(64 * WAVES), lds, s, a);
   return hipGetLastError();
 }

@@ -57,16 +57,16 @@ __device__ inline void rope_angle_cs(int t, float inv_freq, float *c, float *s) 
 }
 
 // Shorter variant for the bf16/fp16 MFMA path (max error ~5e-7, well inside
-// what fp16 operands carry): Cody-Waite reduction by 2 pi in three float32
+// what fp16 operands carry): Cody-Waite reduction by 2 pi in two float32
 // parts (C1 = fl32(2 pi) = 13176795 * 2^-21, so x - k C1 is exact for
-// |x| < 2^20: both terms are multiples of 2^-21, or k = 0), then the
-// hardware sine and cosine units, which take the angle in revolutions.
-// Same domain as fast_sincos.
+// |x| < 2^20: both terms are multiples of 2^-21, or k = 0; the remainder of
+// 2 pi - C1 - C2 is 6.9e-15, so the term dropped is below 1.2e-9 over the
+// domain), then the hardware sine and cosine units, which take the angle in
+// revolutions.  Same domain as fast_sincos.
 __device__ inline void hw_sincos(float x, float *s, float *c) {
   const float k = __builtin_rintf(x * 0.15915493667125702f);
   float r = __builtin_fmaf(-k, 6.2831854820251465f, x);
   r = __builtin_fmaf(-k, -1.7484555314695172e-07f, r);
-  r = __builtin_fmaf(-k, -6.8604980400235275e-15f, r);
   const float rev = r * 0.15915493667125702f;
   *s = __builtin_amdgcn_sinf(rev);
   *c = __builtin_amdgcn_cosf(rev);
