@@ -432,12 +432,12 @@ struct Plan {
 // key ranks up to 256 are prefetched a tile ahead in registers and value
 // ranks up to 512 accumulate in registers.
 static int mfma_lds_bytes(const CellDev &k, const CellDev &v, int d) {
-  const int kpath = 2 * d * (k.rT_pad + 8) + (k.bits > 0 ? 2 * d * (d + 8) : 0);
+  const int kpath = 2 * d * (k.rT_pad + kRowPad) + (k.bits > 0 ? 2 * d * (d + kRowPad) : 0);
   const int waves = v.rT_pad / 16 > 8 ? 4 : 8;
   const int park = waves * (v.rT_pad / 16 + 8) * 512;  // fp16 value partials of every wave
-  // + softmax reduction, frequencies, query operands, combined value tiles
-  // and the token-block counter
-  return std::max(kpath, park) + 1024 + 256 + 4096 + 1024 * (v.rT_pad / 16 + 8) + 16;
+  // + softmax reduction, frequencies (and / 2 pi), query operands, combined
+  // value tiles and the token-block counter
+  return std::max(kpath, park) + 1024 + 512 + 6144 + 1024 * (v.rT_pad / 16 + 8) + 16;
 }
 
 static bool mfma_ok(const jolt_cache *c, int layer, int *lds) {
@@ -623,6 +623,16 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
         }
         ma.nseq = n;
         ma.rV_max = rv;
+        // frequency blocks of 16 whose angles stay below kRopeSmall for every
+        // cached position of the launch's sequences
+        int t_max = 0;
+        for (int i = 0; i < n; ++i) t_max = std::max(t_max, ma.seq[i].T);
+        ma.rope_small = 0;
+        for (int m = 0; m < c0->d / 32; ++m) {
+          double w = 0.0;
+          for (int f = 16 * m; f < 16 * m + 16; ++f) w = std::max(w, (double)inv_freq[f]);
+          if (w * (double)std::max(t_max - 1, 0) <= kRopeSmall) ma.rope_small |= 1 << m;
+        }
         e = jolt_launch_mfma(ma, n, k0.bits, v0.bits, nkt, lds, s);
         if (e != hipSuccess) return fail(JOLT_E_HIP, "split kernel launch: %s", hipGetErrorString(e));
       }

@@ -15,12 +15,17 @@ namespace jolt {
 
 constexpr int kTokPad = 128;    // T padding: one MFMA workgroup tile
 constexpr int kRankPad = 32;    // rank padding: one 16x16x32 MFMA K-step
-constexpr int kRowPad = 8;      // fp16 elements appended to each row of the key-tile
-                                // matrices (W2_K, Pi), which are copied to LDS as they are
+// fp16 elements appended to each row of the key-tile matrices (W2_K, Pi),
+// which are copied to LDS as they are.  With rows of 64 k + 32 bytes the
+// MFMA operand reads (lane (r, g): row r, 16-byte chunk g) reach the full
+// LDS rate on gfx950; strides of 64 k + 16 or 64 k + 48 bytes run at ~57 %
+// of it, multiples of 64 far lower (measured with ds_read_b128).
+constexpr int kRowPad = 16;
 constexpr int kMaxHg = 16;      // query heads per KV head
 constexpr int kMaxBatchPerLaunch = 32;
 constexpr int kMaxD = 128;
 constexpr int kMaxSplits = 2048;
+constexpr double kRopeSmall = 128.0;  // radians; see MfmaArgs::rope_small
 
 // Slot order of a 32-deep MFMA K step built from two 16x16 result tiles:
 // slot q = 8g + j (g = 16-lane group, j = element of the 8-wide operand)
@@ -150,6 +155,9 @@ struct MfmaArgs {
   float scale;
   int32_t q_f32, H, H_q, Hg;
   int32_t n_split, split_tokens, stride, rV_max, nseq;
+  // bit m: every angle t * inv_freq[f] of the launch with 16 m <= f < 16 m + 16
+  // is at most kRopeSmall radians (such blocks skip the 2 pi reduction)
+  int32_t rope_small;
   SeqMfma seq[kMaxBatchPerLaunch];
 };
 static_assert(sizeof(MfmaArgs) <= 4096, "MFMA kernel arguments exceed 4 KiB");
