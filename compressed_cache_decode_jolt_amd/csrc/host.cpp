@@ -73,7 +73,7 @@ static inline float bf16_to_f32(uint16_t h) {
 // --------------------------------------------------------- cache handle --
 struct CellMeta {
   int rT, rF, bits, rT_pad, rF_pad;
-  double a_s;  // keys of bf16 caches: A stored as fp16(A * a_s)
+  double a_s;  // bf16 caches: A stored as fp16(A * a_s)
 };
 
 struct jolt_cache {
@@ -227,12 +227,14 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
         m.rF_pad = round_up(in.r_F, kRankPad);
         c->cells[2 * g + tau] = m;
         Offs &o = offs[2 * g + tau];
-        // A.  Keys of bf16 caches: fp16 scaled by a power of two a_s (exact
-        // for every bf16 value in fp16's normal range) so that the key tile's
-        // MFMA takes A_K rows as they are; W2_K carries the 1 / a_s.
+        // A.  bf16 caches: fp16 scaled by a power of two a_s (exact for every
+        // bf16 value in fp16's normal range) so that the MFMA products take A
+        // as it is -- A_K rows in the key tile, A_V against fp16 softmax
+        // weights (11-bit, where bf16 weights would carry 8); W2 carries the
+        // 1 / a_s.
         o.A = S.take((size_t)fb * T_pad * std::max(m.rT_pad, 1));
         m.a_s = 1.0;
-        const bool a16 = tau == 0 && !f32;
+        const bool a16 = !f32;
         if (a16) {
           float amax = 0.0f;
           for (size_t i = 0; i < (size_t)T * m.rT; ++i)

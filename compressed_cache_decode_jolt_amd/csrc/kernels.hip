@@ -35,7 +35,7 @@ __device__ inline float ldf(const void *p, size_t i) {
     return bf16f(((const uint16_t *)p)[i]);
 }
 
-// A_K element: float32 caches as stored; bf16 caches keep A_K as fp16(A * s).
+// A element (keys or values): float32 caches as stored; bf16 caches keep A as fp16(A * s).
 template <bool F32>
 __device__ inline float ldAk(const CellDev &K, size_t i) {
   if constexpr (F32)
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256) void decode_generic(DecodeArgs a) {
       float acc = 0.0f;
       for (int t = 0; t < nt; ++t) {
         int tg = tt + t;
-        acc += S[u][t] * ldf<F32>(V.A, av_index(tg, r, V.rT_pad));
+        acc += S[u][t] * ldAk<F32>(V, av_index(tg, r, V.rT_pad));
       }
       float *pa = part0 + u * ustride + 4 + r;
       *pa = al_s[u] * *pa + acc;
