@@ -138,6 +138,11 @@ def cpu_baseline(cfg, cache, seconds):
                       f"{cfg.batch} sequences"}
 
 
+def log(msg):
+    """Progress line on stderr (the JSON result is the only stdout line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,10 +192,19 @@ def main():
     torch.cuda.set_device(dev)
 
     # caches: one synthetic cache per sequence, loaded `copies` times
-    host = [gen.synthetic_cache(cfg, allocs[s][1], seq=s) for s in range(B)]
+    host = []
+    for s in range(B):
+        host.append(gen.synthetic_cache(cfg, allocs[s][1], seq=s))
+        log(f"{cfg.name}: synthetic cache {s + 1}/{B} built")
     step_bytes = sum(algorithmic(cfg, allocs[s][1], l)[0] for s in range(B) for l in range(L))
     copies = max(1, math.ceil(2 * MALL_BYTES / step_bytes))
-    caches = [[J.jolt_load_cache(host[s]) for s in range(B)] for _ in range(copies)]
+    caches = []
+    for c in range(copies):
+        caches.append([])
+        for s in range(B):
+            caches[-1].append(J.jolt_load_cache(host[s]))
+            if copies * B <= 64 or s == B - 1:
+                log(f"cache copy {c + 1}/{copies}, sequence {s + 1}/{B} loaded")
     inv = gen.rope_inv_freq_input(cfg.rope_base, d)
     scale = 1.0 / math.sqrt(d)
     qdt = torch.bfloat16 if cfg.q_dtype == "bf16" else torch.float32
@@ -254,6 +268,7 @@ def main():
         torch.cuda.synchronize()
         return g
 
+    log(f"eager: {eager_ms:.4f} ms per step")
     ms_per_step = eager_ms
     graph_ms = None
     if not args.no_graph:
@@ -261,6 +276,7 @@ def main():
         graph_ms = timed_steps(lambda i, t: g.replay() if i is None else step(i, False))
         ms_per_step = graph_ms
         del g
+        log(f"graph: {graph_ms:.4f} ms per step")
 
     per_launch = [[algorithmic(cfg, allocs[s][1], l) for s in range(B)] for l in range(L)]
     bytes_launch = float(np.mean([sum(p[0] for p in pl) for pl in per_launch]))
@@ -310,6 +326,7 @@ def main():
             d_graph = timed_steps(lambda i, t: dg.replay() if i is None else dstep(i))
             dms = d_graph
             del dg
+        log(f"dense: {dms:.4f} ms per step")
         dense = {"ms_per_step": dms, "eager_ms_per_step": d_eager, "graph_ms_per_step": d_graph,
                  "hbm_GBps": dense_step / (dms * 1e-3) / 1e9, "jolt_speedup": dms / ms_per_step}
         del kv

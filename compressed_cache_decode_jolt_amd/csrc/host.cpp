@@ -223,7 +223,9 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
         m.rT = in.r_T;
         m.rF = in.r_F;
         m.bits = in.bits;
-        m.rT_pad = round_up(in.r_T, kRankPad);
+        // ranks above 256 pad to 64, so wide key tiles take an even number of
+        // 32-rank MFMA steps (fewer kernel instantiations)
+        m.rT_pad = round_up(in.r_T, in.r_T > 8 * kRankPad ? 2 * kRankPad : kRankPad);
         m.rF_pad = round_up(in.r_F, kRankPad);
         c->cells[2 * g + tau] = m;
         Offs &o = offs[2 * g + tau];
@@ -434,8 +436,10 @@ struct Plan {
 // key ranks up to 256 are prefetched a tile ahead in registers and value
 // ranks up to 512 accumulate in registers.
 static int mfma_lds_bytes(const CellDev &k, const CellDev &v, int d) {
-  const int kpath = 2 * d * (k.rT_pad + kRowPad) + (k.bits > 0 ? 2 * d * (d + kRowPad) : 0);
-  const int waves = v.rT_pad / 16 > 8 ? 4 : 8;
+  // key ranks above 256 keep Pi in registers (4 waves), not in LDS
+  const bool wide = k.rT_pad > 8 * kRankPad;
+  const int kpath = 2 * d * (k.rT_pad + kRowPad) + (k.bits > 0 && !wide ? 2 * d * (d + kRowPad) : 0);
+  const int waves = wide || v.rT_pad / 16 > 8 ? 4 : 8;
   const int park = waves * (v.rT_pad / 16 + 8) * 512;  // fp16 value partials of every wave
   // + softmax reduction, frequencies (and / 2 pi), query operands, combined
   // value tiles and the token-block counter
@@ -446,7 +450,8 @@ static bool mfma_ok(const jolt_cache *c, int layer, int *lds) {
   if (c->f32 || c->d != 128) return false;
   const LayerDev &L = c->h_layers[layer];
   const CellDev &k = L.c[0], &v = L.c[1];
-  if (v.rT_pad > 512 || k.rT_pad > 256) return false;
+  if (v.rT_pad > 512 || k.rT_pad > 512) return false;
+  if (k.rT_pad > 8 * kRankPad && v.rT_pad > 256) return false;  // no such class
   *lds = mfma_lds_bytes(k, v, c->d);
   return *lds <= jolt_mfma_max_lds();
 }
@@ -496,8 +501,8 @@ static jolt_status plan_decode(const jolt_cache *const *caches, int batch, int l
   }
   if (want == JOLT_KERNEL_MFMA && !mf)
     return fail(JOLT_E_UNSUPPORTED,
-                "MFMA kernel needs bf16 factors, d=128, key rank <= 256, value rank <= 512 and an "
-                "LDS fit for W2_K and Pi");
+                "MFMA kernel needs bf16 factors, d=128, key rank <= 512, value rank <= 512 (<= 256 "
+                "with key ranks above 256) and an LDS fit for W2_K and Pi");
   p->kernel = (want == JOLT_KERNEL_GENERIC || !mf) ? JOLT_KERNEL_GENERIC : JOLT_KERNEL_MFMA;
   const int tile = p->kernel == JOLT_KERNEL_MFMA ? kTokPad : 32;
   int H = batch ? c0->H : 1;

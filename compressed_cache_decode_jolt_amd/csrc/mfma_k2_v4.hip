@@ -19,15 +19,24 @@ static hipError_t go(const jolt::MfmaArgs &a, int nseq, int lds, hipStream_t s) 
 }
 
 // value classes: ranks <= 64 or <= 128 with 8 waves (two per SIMD), <= 512
-// with 4 waves holding the accumulators of 32 rank blocks each
+// with 4 waves holding the accumulators of 32 rank blocks each.  Key ranks
+// above 256 (more than 8 steps; padded to 64, so the step count is even)
+// always run 4 waves: their W2_K fills the LDS and Pi's fragments move to
+// registers; with them, value ranks up to 256.
 template <int KT>
 static hipError_t go_kt(const jolt::MfmaArgs &a, int nseq, int nmv, int lds, hipStream_t s) {
-  if (nmv > 8) return go<KT, 32, 4, 1>(a, nseq, lds, s);
-  if (nmv > 4) return go<KT, 8, 8, 1>(a, nseq, lds, s);
-  return go<KT, 4, 8, 1>(a, nseq, lds, s);
+  if constexpr (KT > 8) {  // value ranks <= 256 (the host sends wider ones elsewhere)
+    if (nmv > 8) return go<KT, 16, 4, 1>(a, nseq, lds, s);
+    if (nmv > 4) return go<KT, 8, 4, 1>(a, nseq, lds, s);
+    return go<KT, 4, 4, 1>(a, nseq, lds, s);
+  } else {
+    if (nmv > 8) return go<KT, 32, 4, 1>(a, nseq, lds, s);
+    if (nmv > 4) return go<KT, 8, 8, 1>(a, nseq, lds, s);
+    return go<KT, 4, 8, 1>(a, nseq, lds, s);
+  }
 }
 
-// nkt: exact key-rank steps of 32 (0..8)
+// nkt: exact key-rank steps of 32 (0..8, 10, 12, 14, 16)
 hipError_t launch_k2_v4(const jolt::MfmaArgs &a, int nseq, int nkt, int nmv, int lds,
                           hipStream_t s) {
   switch (nkt) {
@@ -39,7 +48,12 @@ hipError_t launch_k2_v4(const jolt::MfmaArgs &a, int nseq, int nkt, int nmv, int
     case 5: return go_kt<5>(a, nseq, nmv, lds, s);
     case 6: return go_kt<6>(a, nseq, nmv, lds, s);
     case 7: return go_kt<7>(a, nseq, nmv, lds, s);
-    default: return go_kt<8>(a, nseq, nmv, lds, s);
+    case 8: return go_kt<8>(a, nseq, nmv, lds, s);
+    case 10: return go_kt<10>(a, nseq, nmv, lds, s);
+    case 12: return go_kt<12>(a, nseq, nmv, lds, s);
+    case 14: return go_kt<14>(a, nseq, nmv, lds, s);
+    case 16: return go_kt<16>(a, nseq, nmv, lds, s);
+    default: return hipErrorInvalidValue;  // odd step counts above 8 are never planned
   }
 }
 

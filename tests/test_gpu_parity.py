@@ -204,6 +204,25 @@ def test_mixed_bits_batch_on_mfma(split):
         assert np.max(np.abs(got[b] - want[b])) <= 2e-2
 
 
+WIDE_KEYS = [((320, 64, 0), (64, 32, 2)), ((384, 32, 2), (192, 48, 8)),
+             ((448, 64, 4), (128, 64, 0)), ((512, 96, 8), (64, 32, 4))]
+
+
+@pytest.mark.parametrize("split", [0, 128])
+@pytest.mark.parametrize("aK,aV", WIDE_KEYS, ids=[f"K{k[0]}b{k[2]}-V{v[0]}b{v[2]}" for k, v in WIDE_KEYS])
+def test_wide_key_ranks_on_mfma(aK, aV, split):
+    """Key ranks above 256 (the MHA workload's wide groups): W2_K alone in
+    LDS, Pi's fragments in registers, 4 waves; every residual width."""
+    d, H, H_q, T = 128, 4, 16, 700
+    c = gen.small_cache(90 + aK[0] // 64, T, H, H_q, d, [(aK, aV)], [1])
+    inv = gen.rope_inv_freq_input(5e5, d)
+    q = gen.queries(91, aK[2], aV[2], H_q, d, "bf16")[None]
+    got = run_decode([c], 0, q, [T], inv, 0.088, kernel=J.KERNEL_MFMA, split=split)
+    want = oracle_decode([c], 0, q, [T], inv, 0.088)
+    r, mx = rel_l2(got, want), float(np.max(np.abs(got - want)))
+    assert r <= 5e-3 and mx <= 2e-2, (r, mx)
+
+
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_batch_of_different_lengths_and_ranks(kernel):
     d, H, H_q = 128, 2, 4
