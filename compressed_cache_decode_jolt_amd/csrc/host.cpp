@@ -510,9 +510,28 @@ static jolt_status plan_decode(const jolt_cache *const *caches, int batch, int l
   if (split == 0) {
     // one workgroup per compute unit: the MFMA kernel holds a CU alone
     // (LDS and registers), and fewer, longer splits pay the per-workgroup
-    // prologue and epilogue less often
+    // prologue and epilogue less often.  The MFMA kernel runs one launch per
+    // (key bits, value bits, key-rank steps) class of the batch, one after
+    // the other, so the split count is sized for the smallest class (a
+    // one-sequence class would otherwise fill a fraction of the CUs) and
+    // capped at about four rounds of workgroups for the largest.
     int want_wg = p->kernel == JOLT_KERNEL_MFMA ? cu_count() : 512;
-    int n = std::max(1, (want_wg + batch * H - 1) / std::max(1, batch * H));
+    int units = batch;
+    if (p->kernel == JOLT_KERNEL_MFMA && batch > 1) {
+      int cmin = batch, cmax = 1;
+      for (int i = 0; i < batch; ++i) {
+        const CellDev &ki = caches[i]->h_layers[layer].c[0], &vi = caches[i]->h_layers[layer].c[1];
+        int n = 0;
+        for (int j = 0; j < batch; ++j) {
+          const CellDev &kj = caches[j]->h_layers[layer].c[0], &vj = caches[j]->h_layers[layer].c[1];
+          n += kj.bits == ki.bits && vj.bits == vi.bits && kj.rT_pad == ki.rT_pad;
+        }
+        cmin = std::min(cmin, n);
+        cmax = std::max(cmax, n);
+      }
+      units = std::max(cmin, (cmax + 3) / 4);
+    }
+    int n = std::max(1, (want_wg + units * H - 1) / std::max(1, units * H));
     split = (p->T_max + n - 1) / n;
   }
   p->split_tokens = round_up(std::max(split, 1), tile);
