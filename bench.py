@@ -154,6 +154,9 @@ def main():
     ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "mfma"])
     ap.add_argument("--split-tokens", type=int, default=0, help="tokens per split (0 = auto)")
     ap.add_argument("--dense-split-tokens", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=0,
+                    help="device copies of the caches rotated over the steps (default: enough "
+                         "that a step reads HBM, not the Infinity Cache)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -197,7 +200,7 @@ def main():
         host.append(gen.synthetic_cache(cfg, allocs[s][1], seq=s))
         log(f"{cfg.name}: synthetic cache {s + 1}/{B} built")
     step_bytes = sum(algorithmic(cfg, allocs[s][1], l)[0] for s in range(B) for l in range(L))
-    copies = max(1, math.ceil(2 * MALL_BYTES / step_bytes))
+    copies = args.copies or max(1, math.ceil(2 * MALL_BYTES / step_bytes))
     caches = []
     for c in range(copies):
         caches.append([])
