@@ -615,6 +615,7 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
       ma.n_split = a.n_split;
       ma.split_tokens = a.split_tokens;
       ma.stride = a.stride;
+      ma.grid8 = (a.n_split & 7) == 0;
       bool done[kMaxBatchPerLaunch] = {};
       for (int i0 = 0; i0 < nb; ++i0) {
         if (done[i0]) continue;

@@ -155,6 +155,7 @@ struct MfmaArgs {
   float scale;
   int32_t q_f32, H, H_q, Hg;
   int32_t n_split, split_tokens, stride, rV_max, nseq;
+  int32_t grid8;          // grid (8 H, n_split / 8, nseq) (n_split % 8 == 0), else (H, n_split, nseq)
   // bit m: every angle t * inv_freq[f] of the launch with 16 m <= f < 16 m + 16
   // is at most kRopeSmall radians (such blocks skip the 2 pi reduction)
   int32_t rope_small;

@@ -13,7 +13,8 @@ static hipError_t go(const jolt::MfmaArgs &a, int nseq, int lds, hipStream_t s) 
     if (e != hipSuccess) return e;
     attr = true;
   }
-  dim3 grid((unsigned)(a.n_split * a.H), (unsigned)nseq);
+  const dim3 grid = a.grid8 ? dim3((unsigned)(8 * a.H), (unsigned)(a.n_split / 8), (unsigned)nseq)
+                            : dim3((unsigned)a.H, (unsigned)a.n_split, (unsigned)nseq);
   hipLaunchKernelGGL(k, grid, dim3(64 * WAVES), lds, s, a);
   return hipGetLastError();
 }
