@@ -34,6 +34,28 @@ PEAK_MFMA_BF16 = 2.5e15    # FLOP/s, dense bf16/fp16 MFMA
 MALL_BYTES = 256 << 20
 
 
+_SPIN_CYCLES_PER_MS = None
+
+
+def hold_stream(ms):
+    """Occupy the current stream for about ``ms`` milliseconds with torch's
+    spin kernel (its cycle rate is measured once), so that launches queued
+    behind it start back to back."""
+    import torch
+    global _SPIN_CYCLES_PER_MS
+    if _SPIN_CYCLES_PER_MS is None:
+        n = 1 << 20
+        torch.cuda._sleep(n)  # first launch loads the kernel
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(n)
+        b.record()
+        torch.cuda.synchronize()
+        _SPIN_CYCLES_PER_MS = n / max(a.elapsed_time(b), 1e-3)
+    torch.cuda._sleep(int(min(ms, 5000.0) * _SPIN_CYCLES_PER_MS))
+
+
 class HipEvents:
     """Raw hipEvent_t handles (the library records them on its stream)."""
 
@@ -244,17 +266,28 @@ def main():
         torch.cuda.synchronize()
         return a_.elapsed_time(b_) / args.steps
 
-    # eager: every launch bracketed by HIP events on its stream (kernel time)
+    # eager: one library call per layer from Python
     def eager(i, timed):
         if i is not None:
-            step(i, timed)
+            step(i, False)
         else:
             for k in range(args.steps):
-                step(k, True)
+                step(k, False)
     eager_ms = timed_steps(eager)
+
+    # split-kernel time: the library sets each pair of HIP events to the split
+    # kernel's own start and end.  The steps are queued behind a spin kernel,
+    # so they run back to back as in the graph-replayed step rather than
+    # after idle gaps of the Python loop.
+    torch.cuda.synchronize()
+    hold_stream(3.0 * eager_ms * args.steps + 1.0)
+    for k in range(args.steps):
+        step(k, True)
+    torch.cuda.synchronize()
     split_ms = [ev.elapsed_ms(a, b) for a, b in zip(evb, eve)]
     ev.destroy(evb + eve)
     kern_ms = float(np.mean(split_ms))
+    log(f"split kernel: {kern_ms * 1e3:.2f} us per launch")
 
     def graphed(run_step, n):
         """One HIP graph holding n steps (copies rotate as in eager mode)."""

@@ -456,6 +456,14 @@ static bool mfma_ok(const jolt_cache *c, int layer, int *lds) {
   return *lds <= jolt_mfma_max_lds();
 }
 
+// Two sequences share one MFMA launch when their layer's key bits, value
+// bits and padded key rank match.
+static bool same_class(const jolt_cache *a, const jolt_cache *b, int layer) {
+  const CellDev &ka = a->h_layers[layer].c[0], &va = a->h_layers[layer].c[1];
+  const CellDev &kb = b->h_layers[layer].c[0], &vb = b->h_layers[layer].c[1];
+  return ka.bits == kb.bits && va.bits == vb.bits && ka.rT_pad == kb.rT_pad;
+}
+
 // Compute units of the current device (cached per device).
 static int cu_count() {
   static int cached[64] = {};
@@ -520,12 +528,8 @@ static jolt_status plan_decode(const jolt_cache *const *caches, int batch, int l
     if (p->kernel == JOLT_KERNEL_MFMA && batch > 1) {
       int cmin = batch, cmax = 1;
       for (int i = 0; i < batch; ++i) {
-        const CellDev &ki = caches[i]->h_layers[layer].c[0], &vi = caches[i]->h_layers[layer].c[1];
         int n = 0;
-        for (int j = 0; j < batch; ++j) {
-          const CellDev &kj = caches[j]->h_layers[layer].c[0], &vj = caches[j]->h_layers[layer].c[1];
-          n += kj.bits == ki.bits && vj.bits == vi.bits && kj.rT_pad == ki.rT_pad;
-        }
+        for (int j = 0; j < batch; ++j) n += same_class(caches[j], caches[i], layer);
         cmin = std::min(cmin, n);
         cmax = std::max(cmax, n);
       }
@@ -595,9 +599,10 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
     a.out = out + (size_t)b0 * c0->H_q * c0->d;
     a.ws = (float *)workspace + (size_t)b0 * c0->H_q * p.n_split * p.stride;
     hipError_t e = hipSuccess;
-    if (launch && launch->ev_begin && b0 == 0)
-      e = hipEventRecord((hipEvent_t)launch->ev_begin, s);
-    if (e != hipSuccess) return fail(JOLT_E_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+    // timing events: the first split launch's start and the last one's end
+    KernelEvents ev;
+    if (launch && b0 == 0) ev.begin = (hipEvent_t)launch->ev_begin;
+    hipEvent_t ev_last = launch && b0 + nb >= batch ? (hipEvent_t)launch->ev_end : nullptr;
     if (p.kernel == JOLT_KERNEL_MFMA) {
       // one launch per (key bits, value bits, key-rank steps) class of the
       // chunk's sequences; every launch writes its sequences' rows of the
@@ -617,6 +622,12 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
       ma.stride = a.stride;
       ma.grid8 = (a.n_split & 7) == 0;
       bool done[kMaxBatchPerLaunch] = {};
+      int last_class = 0;  // first member of the chunk's last launch class
+      for (int i0 = 0; i0 < nb; ++i0) {
+        bool first = true;
+        for (int i = 0; i < i0 && first; ++i) first = !same_class(caches[b0 + i], caches[b0 + i0], layer);
+        if (first) last_class = i0;
+      }
       for (int i0 = 0; i0 < nb; ++i0) {
         if (done[i0]) continue;
         const CellDev &k0 = caches[b0 + i0]->h_layers[layer].c[0];
@@ -625,7 +636,7 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
         for (int i = i0; i < nb; ++i) {
           const jolt_cache *c = caches[b0 + i];
           const CellDev &k = c->h_layers[layer].c[0], &v = c->h_layers[layer].c[1];
-          if (done[i] || k.bits != k0.bits || v.bits != v0.bits || k.rT_pad != k0.rT_pad) continue;
+          if (done[i] || !same_class(c, caches[b0 + i0], layer)) continue;
           done[i] = true;
           const LayerDev &L = c->h_layers[layer];
           SeqMfma &m = ma.seq[n];
@@ -660,8 +671,10 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
           for (int f = 16 * m; f < 16 * m + 16; ++f) w = std::max(w, (double)inv_freq[f]);
           if (w * (double)std::max(t_max - 1, 0) <= kRopeSmall) ma.rope_small |= 1 << m;
         }
-        e = jolt_launch_mfma(ma, n, k0.bits, v0.bits, nkt, lds, s);
+        if (i0 == last_class) ev.end = ev_last;
+        e = jolt_launch_mfma(ma, n, k0.bits, v0.bits, nkt, lds, s, ev);
         if (e != hipSuccess) return fail(JOLT_E_HIP, "split kernel launch: %s", hipGetErrorString(e));
+        ev.begin = nullptr;
       }
     } else {
       a.nseq = nb;
@@ -671,13 +684,11 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
         a.seq[i].T = caches[b0 + i]->T;
         a.seq[i].slot = i;
       }
-      e = jolt_launch_generic(a, nb, s);
+      ev.end = ev_last;
+      e = jolt_launch_generic(a, nb, s, ev);
       if (e != hipSuccess) return fail(JOLT_E_HIP, "split kernel launch: %s", hipGetErrorString(e));
     }
     a.nseq = nb;
-    if (launch && launch->ev_end && b0 + nb >= batch)
-      e = hipEventRecord((hipEvent_t)launch->ev_end, s);
-    if (e != hipSuccess) return fail(JOLT_E_HIP, "hipEventRecord: %s", hipGetErrorString(e));
     e = p.kernel == JOLT_KERNEL_MFMA ? jolt_launch_merge_outputs(a, nb, s) : jolt_launch_merge(a, nb, s);
     if (e != hipSuccess) return fail(JOLT_E_HIP, "merge kernel launch: %s", hipGetErrorString(e));
   }

@@ -238,10 +238,19 @@ __device__ inline void stage_rows(uint8_t *dst, int dst_stride, const void *src,
   }
 }
 
+namespace jolt {
+// Optional timing events of a split-kernel launch: a non-null event is set to
+// the launched kernel's own start (begin) or end (end) timestamp.
+struct KernelEvents {
+  hipEvent_t begin = nullptr, end = nullptr;
+};
+}  // namespace jolt
+
 // Kernel launchers (kernels_*.hip).  Each returns the hipError_t of its launch.
-hipError_t jolt_launch_generic(const jolt::DecodeArgs &a, int nseq, hipStream_t s);
+hipError_t jolt_launch_generic(const jolt::DecodeArgs &a, int nseq, hipStream_t s,
+                               jolt::KernelEvents ev);
 hipError_t jolt_launch_mfma(const jolt::MfmaArgs &a, int nseq, int bK, int bV, int nkt,
-                            int lds_bytes, hipStream_t s);
+                            int lds_bytes, hipStream_t s, jolt::KernelEvents ev);
 hipError_t jolt_launch_merge(const jolt::DecodeArgs &a, int nseq, hipStream_t s);
 hipError_t jolt_launch_merge_outputs(const jolt::DecodeArgs &a, int nseq, hipStream_t s);
 hipError_t jolt_launch_dense(const jolt::DenseArgs &a, int nseq, hipStream_t s);

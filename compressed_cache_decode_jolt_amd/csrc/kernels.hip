@@ -10,6 +10,7 @@
 //
 // The generic kernel is plain SIMT (fp32 arithmetic, LDS tiles of 32
 // tokens).  It serves float32 caches and shapes the MFMA kernel does not take.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -759,12 +760,13 @@ hipError_t jolt_launch_sincos(const float *x, int n, float *sn, float *cs, int v
   return hipGetLastError();
 }
 
-hipError_t jolt_launch_generic(const DecodeArgs &a, int nseq, hipStream_t s) {
+hipError_t jolt_launch_generic(const DecodeArgs &a, int nseq, hipStream_t s, KernelEvents ev) {
   dim3 grid(a.n_split, a.H, nseq);
-  if (a.f32)
-    hipLaunchKernelGGL(decode_generic<true>, grid, dim3(256), 0, s, a);
+  auto k = a.f32 ? decode_generic<true> : decode_generic<false>;
+  if (ev.begin || ev.end)  // events take the kernel's own start / end timestamps
+    hipExtLaunchKernelGGL(k, grid, dim3(256), 0u, s, ev.begin, ev.end, 0u, a);
   else
-    hipLaunchKernelGGL(decode_generic<false>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -46,6 +46,16 @@ def stats_table(path, top=8):
     return "\n".join(out)
 
 
+def window_mean(trace, match, start, count):
+    """Mean duration (us) of dispatches start .. start+count-1, in start-time
+    order, of the kernels whose name contains ``match`` (a --kernel-trace CSV)."""
+    rows = [r for r in csv.DictReader(open(trace)) if match in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    sel = rows[start:start + count]
+    assert len(sel) == count, f"only {len(rows)} dispatches of {match!r}"
+    return sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in sel) / count / 1e3
+
+
 def counter_per_dispatch(path, counter, match=None):
     """{kernel name: [value per dispatch]} for one counter of a --pmc CSV."""
     acc = {}
@@ -101,6 +111,9 @@ def main():
     s.add_argument("--title", default="rocprofv3 kernel statistics")
     s.add_argument("--note", default="")
     s.add_argument("--out", required=True)
+    s.add_argument("--trace", default=None, help="kernel-trace CSV for --window")
+    s.add_argument("--window", nargs=3, metavar=("KERNEL", "START", "COUNT"), default=None,
+                   help="also report the mean duration of these dispatches of KERNEL")
     t = sub.add_parser("traffic")
     for k in ("workload", "kernel", "fetch", "write", "calib_fetch", "calib_write", "out"):
         t.add_argument("--" + k.replace("_", "-"), required=True)
@@ -111,7 +124,12 @@ def main():
         text = f"# {a.title}\n\nCommand (from the repository root on one MI355X):\n\n```\n{a.command}\n```\n\n"
         if a.note:
             text += a.note + "\n\n"
-        text += stats_table(a.csv) + "\n\nKernel sources hash: `%s`\n" % kernel_hash()
+        text += stats_table(a.csv) + "\n"
+        if a.window:
+            k, st, n = a.window[0], int(a.window[1]), int(a.window[2])
+            text += ("\nMean duration of `%s` dispatches %d-%d (in start order): %.2f us\n"
+                     % (k, st, st + n - 1, window_mean(a.trace, k, st, n)))
+        text += "\nKernel sources hash: `%s`\n" % kernel_hash()
         open(a.out, "w").write(text)
         print(text)
     else:

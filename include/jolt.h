@@ -94,9 +94,11 @@ typedef struct {
   int32_t kernel;        /* jolt_kernel                                           */
   int32_t split_tokens;  /* tokens per split-T work item (0 = auto); rounded up   */
                          /* to the kernel's tile                                  */
-  void *ev_begin;        /* optional hipEvent_t recorded on the stream right      */
-  void *ev_end;          /* before / after the split-T kernel (NULL = none), so a */
-                         /* caller can time that kernel alone                      */
+  void *ev_begin;        /* optional hipEvent_t (NULL = none), set to the GPU     */
+  void *ev_end;          /* start time of the first split-T kernel launch of the  */
+                         /* call / the end time of its last one (kernel           */
+                         /* timestamps, not stream markers), so a caller can time */
+                         /* the split-T kernels alone                             */
 } jolt_launch;
 
 /*
