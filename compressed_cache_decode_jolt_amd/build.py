@@ -24,6 +24,9 @@ COMMON = [
     "-I", INCLUDE, "-I", CSRC,
     # no packed fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # single-lane atomics stay plain: the atomic optimizer's wave scan waits
+    # for the result at once, which stalls the MFMA kernel's block claim
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wno-unused-command-line-argument",
 ]
 
