@@ -223,6 +223,27 @@ def test_wide_key_ranks_on_mfma(aK, aV, split):
     assert r <= 5e-3 and mx <= 2e-2, (r, mx)
 
 
+ONE_QUERY = [((64, 64, 0), (320, 64, 4)), ((192, 48, 8), (512, 96, 2)),
+             ((256, 64, 2), (144, 32, 8)), ((320, 64, 4), (256, 96, 4)),
+             ((448, 32, 0), (96, 32, 8)), ((512, 96, 8), (48, 32, 0))]
+
+
+@pytest.mark.parametrize("split", [0, 128])
+@pytest.mark.parametrize("aK,aV", ONE_QUERY, ids=[f"K{k[0]}b{k[2]}-V{v[0]}b{v[2]}" for k, v in ONE_QUERY])
+def test_one_query_per_kv_head_on_mfma(aK, aV, split):
+    """One query per KV head (the MHA workload's shape) in the 4-wave
+    classes: value ranks above 128, and key ranks above 256 with value ranks
+    up to 256; the value products run as dot products on the VALU."""
+    d, H, H_q, T = 128, 4, 4, 700
+    c = gen.small_cache(120 + aK[0] // 32 + aV[0] // 16, T, H, H_q, d, [(aK, aV)], [1])
+    inv = gen.rope_inv_freq_input(1e4, d)
+    q = gen.queries(121, aK[2], aV[2], H_q, d, "bf16")[None]
+    got = run_decode([c], 0, q, [T], inv, 0.088, kernel=J.KERNEL_MFMA, split=split)
+    want = oracle_decode([c], 0, q, [T], inv, 0.088)
+    r, mx = rel_l2(got, want), float(np.max(np.abs(got - want)))
+    assert r <= 5e-3 and mx <= 2e-2, (r, mx)
+
+
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_batch_of_different_lengths_and_ranks(kernel):
     d, H, H_q = 128, 2, 4
