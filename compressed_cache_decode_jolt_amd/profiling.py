@@ -16,17 +16,28 @@ import csv
 import hashlib
 import json
 import os
+import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 
+def _code_only(text):
+    """C/C++ source without comments and with whitespace runs collapsed, so
+    that an edit of a comment does not change the hash of the code."""
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    return " ".join(text.split())
+
+
 def kernel_hash():
-    """Hash of the HIP sources (kernels, headers, includes)."""
+    """Hash of the HIP sources (kernels, headers, includes), comments and
+    whitespace aside."""
     h = hashlib.sha256()
     csrc = os.path.join(PKG, "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h", ".inc")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            h.update(f.encode() + b"\0")
+            h.update(_code_only(open(os.path.join(csrc, f)).read()).encode())
     return h.hexdigest()[:16]
 
 
