@@ -225,7 +225,8 @@ def test_wide_key_ranks_on_mfma(aK, aV, split):
 
 ONE_QUERY = [((64, 64, 0), (320, 64, 4)), ((192, 48, 8), (512, 96, 2)),
              ((256, 64, 2), (144, 32, 8)), ((320, 64, 4), (256, 96, 4)),
-             ((448, 32, 0), (96, 32, 8)), ((512, 96, 8), (48, 32, 0))]
+             ((448, 32, 0), (96, 32, 8)), ((512, 96, 8), (48, 32, 0)),
+             ((384, 64, 2), (0, 0, 8)), ((128, 64, 0), (0, 0, 4))]
 
 
 @pytest.mark.parametrize("split", [0, 128])
@@ -242,6 +243,26 @@ def test_one_query_per_kv_head_on_mfma(aK, aV, split):
     want = oracle_decode([c], 0, q, [T], inv, 0.088)
     r, mx = rel_l2(got, want), float(np.max(np.abs(got - want)))
     assert r <= 5e-3 and mx <= 2e-2, (r, mx)
+
+
+@pytest.mark.parametrize("split", [0, 256])
+def test_one_query_batch_of_mixed_classes(split):
+    """One query per KV head, one batch whose sequences fall in different
+    launch classes (8 waves; 4 waves with value ranks above 128, two token
+    blocks per step; 4 waves with key ranks above 256) and lengths."""
+    d, H, H_q = 128, 4, 4
+    spec = [(300, (96, 64, 4), (64, 32, 2)), (1000, (160, 64, 8), (400, 96, 4)),
+            (400, (352, 96, 2), (128, 64, 8)), (513, (96, 64, 4), (64, 32, 2))]
+    caches = [gen.small_cache(130 + i, T, H, H_q, d, [(aK, aV)], [1])
+              for i, (T, aK, aV) in enumerate(spec)]
+    inv = gen.rope_inv_freq_input(1e4, d)
+    q = np.stack([gen.queries(131, i, 0, H_q, d, "bf16") for i in range(len(spec))])
+    q_pos = [T for T, _, _ in spec]
+    got = run_decode(caches, 0, q, q_pos, inv, 0.088, kernel=J.KERNEL_MFMA, split=split)
+    want = oracle_decode(caches, 0, q, q_pos, inv, 0.088)
+    for b in range(len(spec)):
+        assert rel_l2(got[b], want[b]) <= 5e-3, (b, rel_l2(got[b], want[b]))
+        assert np.max(np.abs(got[b] - want[b])) <= 2e-2
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
