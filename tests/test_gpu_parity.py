@@ -245,6 +245,23 @@ def test_one_query_per_kv_head_on_mfma(aK, aV, split):
     assert r <= 5e-3 and mx <= 2e-2, (r, mx)
 
 
+@pytest.mark.parametrize("H,H_q,aK,aV", [(2, 8, (96, 64, 4), (64, 32, 4)),
+                                         (4, 4, (320, 64, 8), (160, 64, 2))],
+                         ids=["group4", "one-query-wide"])
+def test_fp32_queries_on_mfma(H, H_q, aK, aV):
+    """float32 queries (converted in the kernel's prologue) at a decode
+    position past the cache's end, on an 8-wave class and a one-query
+    4-wave class."""
+    d, T = 128, 600
+    c = gen.small_cache(140 + H, T, H, H_q, d, [(aK, aV)], [1])
+    inv = gen.rope_inv_freq_input(5e5, d)
+    q = gen.queries(141, H, 0, H_q, d, "f32")[None]
+    got = run_decode([c], 0, q, [T + 37], inv, 0.088, q_dtype="f32", kernel=J.KERNEL_MFMA)
+    want = oracle_decode([c], 0, q, [T + 37], inv, 0.088)
+    r, mx = rel_l2(got, want), float(np.max(np.abs(got - want)))
+    assert r <= 5e-3 and mx <= 2e-2, (r, mx)
+
+
 @pytest.mark.parametrize("split", [0, 256])
 def test_one_query_batch_of_mixed_classes(split):
     """One query per KV head, one batch whose sequences fall in different
