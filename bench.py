@@ -56,6 +56,44 @@ def hold_stream(ms):
     torch.cuda._sleep(int(min(ms, 5000.0) * _SPIN_CYCLES_PER_MS))
 
 
+def achievable_peak(bound, dev):
+    """A measured ceiling on this GPU for the roofline's bound, beside the
+    published peak: a bf16 matrix product through torch.matmul (8192^3,
+    hipBLASLt) for "mfma", a 1 GiB device-to-device copy (read + write
+    bytes) for "hbm".  Calibration only; nothing of the decode path runs
+    through it."""
+    import torch
+    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if bound == "mfma":
+        n, reps = 8192, 10
+        x = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+        y = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+        for _ in range(3):
+            z = x @ y
+        torch.cuda.synchronize()
+        a_.record()
+        for _ in range(reps):
+            z = x @ y
+        b_.record()
+        torch.cuda.synchronize()
+        del x, y, z
+        return 2.0 * n ** 3 * reps / (a_.elapsed_time(b_) * 1e-3) / 1e12, \
+            "torch.matmul bf16 8192x8192x8192"
+    n, reps = 1 << 30, 10
+    src = torch.ones(n // 2, device=dev, dtype=torch.bfloat16)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a_.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b_.record()
+    torch.cuda.synchronize()
+    del src, dst
+    return 2.0 * n * reps / (a_.elapsed_time(b_) * 1e-3) / 1e9, "device copy of 1 GiB (read + write)"
+
+
 class HipEvents:
     """Raw hipEvent_t handles (the library records them on its stream)."""
 
@@ -185,6 +223,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (default: the timed steps are also captured "
                          "in one HIP graph and replayed; value comes from the replay)")
+    ap.add_argument("--no-achievable", action="store_true",
+                    help="skip the measured-ceiling probe reported beside the published peak")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -332,6 +372,11 @@ def main():
     roof["kernel_ms"] = kern_ms
     roof["alg_bytes_per_launch"] = bytes_launch
     roof["alg_flops_per_launch"] = flops_launch
+    if not args.no_achievable:
+        ceil, probe = achievable_peak(roof["bound"], dev)
+        roof["achievable"] = {"peak": ceil, "unit": roof["unit"], "frac": achieved / ceil,
+                              "probe": probe}
+        log(f"achievable {roof['bound']} ceiling: {ceil:.1f} {roof['unit']} ({probe})")
 
     # dense comparator on the same shape (random bf16 post-RoPE K and V)
     dense = None
