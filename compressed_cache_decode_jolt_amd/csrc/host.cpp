@@ -435,12 +435,18 @@ struct Plan {
 // tile loop the W2_K / Pi region holds every wave's fp16 value partial;
 // key ranks up to 256 are prefetched a tile ahead in registers and value
 // ranks up to 512 accumulate in registers.
-static int mfma_lds_bytes(const CellDev &k, const CellDev &v, int d) {
+// hg1: one query per KV head.  The classes launched as HG1 variants (value
+// ranks above 128, or key ranks above 256) park 4 lanes' worth of each value
+// block per wave instead of 64, and with key ranks up to 256 run 8 waves.
+static int mfma_lds_bytes(const CellDev &k, const CellDev &v, int d, bool hg1) {
   // key ranks above 256 keep Pi in registers (4 waves), not in LDS
   const bool wide = k.rT_pad > 8 * kRankPad;
   const int kpath = 2 * d * (k.rT_pad + kRowPad) + (k.bits > 0 && !wide ? 2 * d * (d + kRowPad) : 0);
-  const int waves = wide || v.rT_pad / 16 > 8 ? 4 : 8;
-  const int park = waves * (v.rT_pad / 16 + 8) * 512;  // fp16 value partials of every wave
+  const bool big_v = v.rT_pad / 16 > 8;
+  const bool hg1v = hg1 && (wide || big_v);  // launched as an HG1 variant
+  const int waves = wide || (big_v && !hg1v) ? 4 : 8;
+  // fp16 value partials of every wave
+  const int park = waves * (v.rT_pad / 16 + 8) * (hg1v ? 32 : 512);
   // + softmax reduction, frequencies (and / 2 pi), query operands, combined
   // value tiles and the token-block counter
   return std::max(kpath, park) + 1024 + 512 + 6144 + 1024 * (v.rT_pad / 16 + 8) + 16;
@@ -452,7 +458,7 @@ static bool mfma_ok(const jolt_cache *c, int layer, int *lds) {
   const CellDev &k = L.c[0], &v = L.c[1];
   if (v.rT_pad > 512 || k.rT_pad > 512) return false;
   if (k.rT_pad > 8 * kRankPad && v.rT_pad > 256) return false;  // no such class
-  *lds = mfma_lds_bytes(k, v, c->d);
+  *lds = mfma_lds_bytes(k, v, c->d, c->H_q == c->H);
   return *lds <= jolt_mfma_max_lds();
 }
 
@@ -657,7 +663,7 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
           ++n;
           nkt = k.rT_pad / kRankPad;
           rv = std::max(rv, v.rT_pad);
-          lds = std::max(lds, mfma_lds_bytes(k, v, c->d));
+          lds = std::max(lds, mfma_lds_bytes(k, v, c->d, c->H_q == c->H));
         }
         ma.nseq = n;
         ma.rV_max = rv;
