@@ -262,6 +262,26 @@ def test_fp32_queries_on_mfma(H, H_q, aK, aV):
     assert r <= 5e-3 and mx <= 2e-2, (r, mx)
 
 
+@pytest.mark.parametrize("split", [512, 1024])
+def test_two_blocks_per_step_on_short_key_chains(split):
+    """Key ranks up to 64 with long splits take two 16-token blocks per wave
+    step; a batch of such classes (ragged lengths, a split's last step half
+    empty) against the oracle."""
+    d, H, H_q = 128, 2, 8
+    spec = [(1500, (48, 32, 4), (64, 32, 2)), (1111, (20, 16, 8), (40, 32, 4)),
+            (900, (0, 0, 4), (64, 48, 8)), (1500, (64, 64, 2), (16, 16, 0))]
+    caches = [gen.small_cache(150 + i, T, H, H_q, d, [(aK, aV)], [1])
+              for i, (T, aK, aV) in enumerate(spec)]
+    inv = gen.rope_inv_freq_input(5e5, d)
+    q = np.stack([gen.queries(151, i, 0, H_q, d, "bf16") for i in range(len(spec))])
+    q_pos = [T for T, _, _ in spec]
+    got = run_decode(caches, 0, q, q_pos, inv, 0.088, kernel=J.KERNEL_MFMA, split=split)
+    want = oracle_decode(caches, 0, q, q_pos, inv, 0.088)
+    for b in range(len(spec)):
+        assert rel_l2(got[b], want[b]) <= 5e-3, (b, rel_l2(got[b], want[b]))
+        assert np.max(np.abs(got[b] - want[b])) <= 2e-2
+
+
 @pytest.mark.parametrize("split", [0, 256])
 def test_one_query_batch_of_mixed_classes(split):
     """One query per KV head, one batch whose sequences fall in different
