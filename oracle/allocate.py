@@ -1,15 +1,15 @@
 """Joint rank/bit allocation under a global byte budget with one Lagrange
 multiplier.
 
-"A JoLT for the KV cache" (arXiv 2607.12550v4 summary), §3 Method: the
-allocator minimises summed reconstruction error subject to a global byte
-budget, choosing ranks and residual bits jointly; its surrogate multiplies the
-discarded-mass estimate by the fraction the rotated quantiser leaves
-unrecovered; the coordinate-wise rank search is a heuristic over the two
-truncated modes; a token-rank cap guards against over-buying key rank.  The
-gist.science summaries ("Gezamenlijke Lagrangian Allocatie") state the single
-dual variable, the objective (total reconstruction error under a global byte
-budget) and the granularity (per layer group, keys and values separately).
+What this module computes: for every cell (layer group, K or V) a triple
+(r_T, r_F, b) that minimises the summed estimated squared reconstruction error
+of all cells subject to one total byte limit, by pricing bytes with a single
+multiplier lambda and bisecting lambda until the limit is met.  Sources: "A
+JoLT for the KV cache" (arXiv 2607.12550v4 summary), §3 Method (the
+allocator, its error surrogate, the coordinate-wise rank search and the
+token-rank cap) and the gist.science summaries, section "Gezamenlijke
+Lagrangian Allocatie" (one dual variable; granularity per layer group with
+keys and values as separate cells).
 
 Readings taken where the pages are silent:
 

@@ -1,11 +1,13 @@
 """Decode attention over a JoLT-compressed cache, and dense decode attention.
 
-"A JoLT for the KV cache" (arXiv 2607.12550v4 summary), Abstract and §4.5:
-the decode kernel evaluates attention directly over the stored factors and
-packed residuals; keys need full reconstruction because RoPE does not commute
-with the factorisation.  Whatever the kernel does, the value it computes is
-plain softmax attention of the RoPE'd query over the decoded cache, which is
-what this module writes out:
+TEST INFRASTRUCTURE (see the package docstring).  What this module computes:
+the plain definition of one decode step's attention over the cache that the
+stored cells decode to (factors plus de-rotated residual).  A fused kernel
+that works on the factors directly evaluates the same quantity in another
+order, so it must produce the same numbers.  Source: "A JoLT for the KV
+cache" (arXiv 2607.12550v4 summary), Abstract and §4.5 (fused decode over
+stored factors and packed residuals; key tiles rebuilt because RoPE and the
+factorisation do not commute).  Written out:
 
   K^[l, h] = A_K G_K[l', h] B_K^T + [b_K > 0] deq(codes_K[l', h]) Pi^T  (V^ alike)
   s_t      = scale * rope(q_j, q_pos) . rope(K^[l, h]_t, t)

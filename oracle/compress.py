@@ -1,12 +1,12 @@
 """The JoLT compressor: grouped prefill cache -> stored cells.
 
-"A JoLT for the KV cache" (arXiv 2607.12550v4 summary), Abstract and §3:
-partial Tucker along the token and feature modes of each grouped cache
-(tucker.st_hosvd), the truncation residual R = X - X~ stored after a seeded
-feature-axis rotation and uniform b-bit quantisation (rotation, quant), ranks
-and bits chosen per cell by one Lagrange multiplier under a global byte
-budget (allocate).  The gist.science summaries ("JL-Geroteerd Residu") define
-the residual as R = X - X~.
+What this module computes: for each cell, the ST-HOSVD factors
+(tucker.st_hosvd) rounded to the storage dtype, the residual X - X~ of that
+stored reconstruction rotated by Pi (rotation) and quantised to b bits with
+its codes packed (quant); the ranks and bits come from the single-multiplier
+allocator (allocate).  Sources: "A JoLT for the KV cache" (arXiv
+2607.12550v4 summary), Abstract and §3; the gist.science summaries, section
+"JL-Geroteerd Residu" (R = X - X~).
 
 Reading taken: X~ is the reconstruction from the *stored* (dtype-rounded)
 factors, so the residual also absorbs factor rounding -- the decoder adds the

@@ -1,11 +1,12 @@
 """Rotary position embedding at float32 angles.
 
-The sarnas.ru JoLT post (section on why cos/sin are built inside the kernel)
-passes the model's own inv_freq (d/2 float32 values) and builds cos/sin in
-float32 from int32 token positions, float32 being required because angles
-reach ~1e5 rad at 128K.  "A JoLT for the KV cache" (arXiv 2607.12550v4
-summary) §3 decomposes keys before RoPE and §4.5/§5 re-apply it per tile
-because RoPE does not commute with the factorisation.
+What this module computes: the rotation of a query or key vector to its
+token position, with the angle of each feature pair formed in float32 from
+the model's float32 inverse frequencies and an integer position.  Sources: the
+sarnas.ru JoLT post (section on building cos/sin inside the kernel: float32
+angles from int32 positions and the model's inv_freq) and "A JoLT for the KV
+cache" (arXiv 2607.12550v4 summary), §3 and §4.5/§5 (keys decomposed before
+RoPE, RoPE applied again per decoded tile).
 
 Reading taken: rotate-half pairing (feature i with i + d/2), as in the Llama
 family; the angle of pair i at position t is the float32 product

@@ -1,10 +1,12 @@
 """The seeded random orthogonal (JL) rotation of the residual.
 
-"A JoLT for the KV cache" (arXiv 2607.12550v4 summary), §1 and §3: the
-truncation residual is stored after a random orthogonal rotation along the
-feature axis; the rotation is seeded, shared by all cells and regenerated at
-decode.  The gist.science summaries (section "JL-Geroteerd Residu") describe
-the decoder as inverting the rotation.
+What this module computes: one d x d orthogonal matrix Pi per cache, built
+deterministically from the cache's rotation seed, that maps each residual row
+into the basis where it is quantised (and back, by its transpose).  Sources:
+"A JoLT for the KV cache" (arXiv 2607.12550v4 summary), §1 and §3 (seeded
+feature-axis rotation common to all cells, rebuilt by the decoder); the
+gist.science summaries, section "JL-Geroteerd Residu" (decoding undoes the
+rotation).
 
 Reading taken (the pages name no distribution or generator): Pi is a
 Haar-distributed d x d orthogonal matrix obtained as the QR factor of a

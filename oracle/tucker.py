@@ -1,13 +1,13 @@
 """Partial Tucker decomposition of a grouped KV cache by ST-HOSVD.
 
-"A JoLT for the KV cache" (arXiv 2607.12550v4 summary), §3 Method: each key
-or value cache of a layer group is a fourth-order tensor (layers x heads x
-tokens x features); JoLT truncates the token and feature modes and keeps the
-layer and head modes at full rank; the token and feature bases are shared by
-all heads and layers of the group; token truncation precedes feature
-truncation.  The Dutch and French gist.science technical summaries (section
-"Partiële Tucker Decompositie" / "Décomposition de Tucker Partielle") name the
-algorithm: sequentially truncated higher-order SVD (ST-HOSVD).
+What this module computes: for one cell, the layer-group cache viewed as a
+4-way array (layers, heads, tokens, features), an orthonormal token basis A
+and feature basis B common to every layer and head of the group, and a core
+G[l, h] per layer and head, by sequentially truncated HOSVD -- the token mode
+first, then the feature mode of the token-projected array; the layer and head
+modes are left untruncated.  Sources: "A JoLT for the KV cache" (arXiv
+2607.12550v4 summary), §3 Method; the gist.science summaries, section
+"Partiële Tucker Decompositie" / "Décomposition de Tucker Partielle".
 
 Tensor layout: X[l, h, t, f] with shape (|g|, H, T, d).
 

@@ -3,6 +3,7 @@
 import json
 import os
 
+import numpy as np
 import pytest
 
 from oracle.accounting import cache_bytes, cell_bytes, dense_kv_bytes
@@ -50,3 +51,48 @@ def test_cache_bytes_sums_cells():
     want = (cell_bytes(64, 32, 2, 2, 16, 16, 2, 2) + cell_bytes(64, 32, 2, 2, 32, 16, 0, 2)
             + cell_bytes(64, 32, 1, 2, 0, 0, 8, 2) + cell_bytes(64, 32, 1, 2, 16, 32, 4, 2))
     assert cache_bytes(cache) == want
+
+
+def stored_bytes(cache):
+    """Bytes of the arrays oracle.compress.compress actually stores, each in
+    its storage dtype: A, B, G at the factor dtype's size per element, the
+    packed codes as uint8 and one float32 scale per quantised row."""
+    fb = {"bf16": 2, "f32": 4}[cache["factor_dtype"]]
+    total = 0
+    for pair in cache["cells"]:
+        for cell in pair:
+            total += fb * (cell["A"].size + cell["B"].size + cell["G"].size)
+            if cell["codes"] is not None:
+                assert cell["codes"].dtype == np.uint8 and cell["scales"].dtype == np.float32
+                total += cell["codes"].nbytes + cell["scales"].nbytes
+    return total
+
+
+@pytest.mark.parametrize("factor_dtype", ["bf16", "f32"])
+def test_cache_bytes_equals_stored_arrays(factor_dtype):
+    """O10 against what the compressor really stores (several layers per
+    group, several heads, every residual width, a rank-0 cell), not against
+    a restatement of the formula."""
+    from oracle.compress import compress
+    from workloads import gen
+
+    T, d, H = 48, 32, 3
+    sizes = [2, 1, 3]
+    alloc = [((16, 16, 0), (32, 16, 2)), ((0, 0, 4), (16, 32, 8)), ((32, 32, 8), (0, 0, 0))]
+    groups = []
+    for g, gs in enumerate(sizes):
+        groups.append(tuple(gen.kv_tensor((97, 0, g, tau), gs, H, T, d, 1.0 - 0.6 * tau, tau == 0, 1,
+                                          rank=8) for tau in (0, 1)))
+    starts = list(np.cumsum([0] + sizes))
+    cache = compress(groups, alloc, factor_dtype, 11, 2 * H, starts)
+    assert stored_bytes(cache) == cache_bytes(cache)
+    # and per cell: the stored shapes are the ones O10 counts
+    for (gK, gV), gs, (aK, aV) in zip(cache["cells"], sizes, alloc):
+        for cell, (rT, rF, b) in ((gK, aK), (gV, aV)):
+            assert cell["A"].shape == (T, rT) and cell["B"].shape == (d, rF)
+            assert cell["G"].shape == (gs, H, rT, rF)
+            if b:
+                assert cell["codes"].shape == (gs, H, T, d * b // 8)
+                assert cell["scales"].shape == (gs, H, T)
+            else:
+                assert cell["codes"] is None and cell["scales"] is None

@@ -106,3 +106,71 @@ def test_keys_cheaper_than_values():
     cells = small_cells(3)
     choice, _ = al.allocate(cells, budget_for(3.0, 1, 2, 32, 64))
     assert cells[1].bytes(*choice[1]) >= cells[0].bytes(*choice[0])
+
+
+# ------------------------------------------------- discarded-mass tails --
+# The surrogate's tails are pinned against the true error of the ST-HOSVD the
+# compressor runs (oracle.tucker.st_hosvd, itself pinned by Eckart-Young and
+# the ST-HOSVD error identity), never against a restatement of their own
+# cumulative sums.
+from oracle.tucker import st_hosvd  # noqa: E402
+
+
+def true_err2(X, rT, rF):
+    A, B, G = st_hosvd(X, rT, rF)
+    return float(np.sum((X - reconstruct(A, B, G)) ** 2))
+
+
+def test_tail_T_is_eckart_young_error():
+    """One layer, one head, full feature rank: ST-HOSVD is the rank-r_T
+    truncated SVD, whose squared error is exactly the discarded token mass."""
+    X = gen.kv_tensor((96, 0, 0, 1), 1, 1, 80, 32, 0.3, False, 0, rank=24)
+    st = cell_stats(X, 2)
+    for r in range(0, 81, 16):
+        e = true_err2(X, r, 32) if r else float(np.sum(X ** 2))
+        assert float(st.tail_T(r)) == pytest.approx(e, rel=1e-9, abs=1e-9 * st.norm2), r
+    # the same through the surrogate at b = 0 (phi = 1)
+    for r in (16, 48):
+        assert float(st.surrogate(r, 32, 0)) == pytest.approx(true_err2(X, r, 32), rel=1e-9)
+
+
+def test_tail_F_is_eckart_young_error():
+    """Full token rank: ST-HOSVD truncates only the feature mode, and the
+    error is exactly the discarded feature mass of the unprojected tensor."""
+    X = gen.kv_tensor((96, 1, 0, 0), 2, 2, 40, 32, 1.0, True, 2, rank=12)
+    st = cell_stats(X, 2)
+    full_T = min(40, 2 * 2 * 32)
+    for r in (8, 16, 24):
+        assert float(st.tail_F(r)) == pytest.approx(true_err2(X, full_T, r), rel=1e-9)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_surrogate_brackets_true_st_hosvd_error(seed):
+    """General (r_T, r_F): the true squared error lies between the larger of
+    the two tails (each mode alone is an Eckart-Young lower bound) and their
+    sum (the ST-HOSVD bound the surrogate prices), and the surrogate at
+    b = 0 is never below it."""
+    g = np.random.default_rng(seed)
+    gs, H, T, d = 2, 3, 64, 32
+    X = gen.kv_tensor((95, seed, 0, seed & 1), gs, H, T, d, [1.0, 0.3][seed & 1], True, 2, rank=20)
+    st = cell_stats(X, 2)
+    for _ in range(6):
+        rT = int(g.integers(1, 5)) * 16
+        rF = int(g.integers(1, 3)) * 16
+        e = true_err2(X, rT, rF)
+        lo = max(float(st.tail_T(rT)), float(st.tail_F(rF)))
+        hi = float(st.tail_T(rT) + st.tail_F(rF))
+        tol = 1e-10 * st.norm2          # rounding of norm2 - cumsum
+        assert lo - tol <= e <= hi + tol, (rT, rF, lo, e, hi)
+        assert float(st.surrogate(rT, rF, 0)) >= e - tol
+
+
+def test_tails_fail_on_an_index_shift():
+    """An off-by-one in the cumulative-sum index would move every tail by a
+    whole squared singular value: the Eckart-Young case tells them apart."""
+    X = gen.kv_tensor((96, 2, 0, 1), 1, 1, 64, 32, 0.3, False, 0, rank=24)
+    st = cell_stats(X, 2)
+    e = true_err2(X, 16, 32)
+    assert float(st.tail_T(16)) == pytest.approx(e, rel=1e-9)
+    assert abs(float(st.tail_T(16)) - (st.norm2 - np.sum(st.sT2[:15]))) > 1e-3 * e
+    assert abs(float(st.tail_T(16)) - (st.norm2 - np.sum(st.sT2[:17]))) > 1e-3 * e
