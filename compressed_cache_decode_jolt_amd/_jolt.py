@@ -39,7 +39,8 @@ class jolt_cache_desc(C.Structure):
 
 class jolt_launch(C.Structure):
     _fields_ = [("kernel", C.c_int32), ("split_tokens", C.c_int32),
-                ("ev_begin", C.c_void_p), ("ev_end", C.c_void_p)]
+                ("ev_begin", C.c_void_p), ("ev_end", C.c_void_p),
+                ("deterministic", C.c_int32)]
 
 
 _lib = None
@@ -100,11 +101,11 @@ def _stream(stream):
     return C.c_void_p(stream.cuda_stream)
 
 
-def _launch(kernel=None, split_tokens=0, events=None):
-    if kernel is None and not split_tokens and events is None:
+def _launch(kernel=None, split_tokens=0, events=None, deterministic=False):
+    if kernel is None and not split_tokens and events is None and not deterministic:
         return None
     ev = events or (None, None)
-    return jolt_launch(int(kernel or 0), int(split_tokens), ev[0], ev[1])
+    return jolt_launch(int(kernel or 0), int(split_tokens), ev[0], ev[1], int(bool(deterministic)))
 
 
 def _factor_bytes(x, dtype):
@@ -211,20 +212,64 @@ def _dtype_code(t):
     raise TypeError(t.dtype)
 
 
+def _check_tensor(name, t, dtypes, shape):
+    """Shape, dtype, device and layout rules of a device tensor argument (the
+    library takes raw pointers and cannot check them itself)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _inv_freq(inv_freq, d):
+    inv = np.ascontiguousarray(inv_freq, dtype=np.float32).ravel()
+    if inv.size < d // 2:
+        raise ValueError(f"inv_freq has {inv.size} values, needs d/2 = {d // 2}")
+    return inv
+
+
+def _workspace(ws):
+    import torch
+    if ws is None:
+        return ws
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return ws
+
+
 def jolt_decode_attention(caches, layer, q, q_pos, inv_freq, softmax_scale, out, workspace,
-                          kernel=None, split_tokens=0, stream=None, events=None):
+                          kernel=None, split_tokens=0, stream=None, events=None,
+                          deterministic=False):
     """q: device tensor [B, H_q, d] (f32/bf16); out: device f32 [B, H_q, d];
     workspace: device tensor of at least jolt_decode_workspace_size bytes;
     events: optional (begin, end) raw hipEvent_t handles recorded around the
-    split-T kernel."""
+    split-T kernel; deterministic: fixed block schedule (bitwise repeatable)."""
+    import torch
     B = len(caches)
+    if B:
+        m = caches[0].meta
+        shape = (B, m["H_q"], m["d"])
+        _check_tensor("q", q, (torch.float32, torch.bfloat16), shape)
+        _check_tensor("out", out, (torch.float32,), shape)
+        if len(q_pos) != B:
+            raise ValueError(f"q_pos has {len(q_pos)} entries for {B} sequences")
+        inv = _inv_freq(inv_freq, m["d"])
+    else:
+        inv = np.zeros(1, dtype=np.float32)
     qp = (C.c_int32 * max(1, B))(*[int(x) for x in q_pos])
-    inv = np.ascontiguousarray(inv_freq, dtype=np.float32)
-    L = _launch(kernel, split_tokens, events)
+    L = _launch(kernel, split_tokens, events, deterministic)
     _check(lib().jolt_decode_attention(
         _handles(caches), B, layer, _ptr(q), _dtype_code(q), qp,
         inv.ctypes.data_as(C.POINTER(C.c_float)), C.c_float(softmax_scale), _ptr(out),
-        _ptr(workspace), _nbytes(workspace), C.byref(L) if L else None, _stream(stream)))
+        _ptr(_workspace(workspace)), _nbytes(workspace), C.byref(L) if L else None,
+        _stream(stream)))
 
 
 def jolt_dense_workspace_size(batch, n_kv, n_q, d, T, kernel=None, split_tokens=0):
@@ -238,14 +283,22 @@ def jolt_dense_workspace_size(batch, n_kv, n_q, d, T, kernel=None, split_tokens=
 def jolt_dense_attention(k_rope, v, q, q_pos, inv_freq, softmax_scale, out, workspace,
                          split_tokens=0, stream=None):
     """k_rope, v: device [B, H, T, d] (f32/bf16); q: [B, H_q, d]; out f32."""
+    import torch
     B, H, T, d = k_rope.shape
+    Hq = q.shape[1]
+    _check_tensor("k_rope", k_rope, (torch.float32, torch.bfloat16), (B, H, T, d))
+    _check_tensor("v", v, (k_rope.dtype,), (B, H, T, d))
+    _check_tensor("q", q, (torch.float32, torch.bfloat16), (B, Hq, d))
+    _check_tensor("out", out, (torch.float32,), (B, Hq, d))
+    if len(q_pos) != B:
+        raise ValueError(f"q_pos has {len(q_pos)} entries for {B} sequences")
     qp = (C.c_int32 * max(1, B))(*[int(x) for x in q_pos])
-    inv = np.ascontiguousarray(inv_freq, dtype=np.float32)
+    inv = _inv_freq(inv_freq, d)
     L = _launch(None, split_tokens)
     _check(lib().jolt_dense_attention(
-        _ptr(k_rope), _ptr(v), _dtype_code(k_rope), B, H, q.shape[1], d, T, _ptr(q),
+        _ptr(k_rope), _ptr(v), _dtype_code(k_rope), B, H, Hq, d, T, _ptr(q),
         _dtype_code(q), qp, inv.ctypes.data_as(C.POINTER(C.c_float)), C.c_float(softmax_scale),
-        _ptr(out), _ptr(workspace), _nbytes(workspace), C.byref(L) if L else None,
+        _ptr(out), _ptr(_workspace(workspace)), _nbytes(workspace), C.byref(L) if L else None,
         _stream(stream)))
 
 

@@ -15,10 +15,6 @@
 #include "jolt.h"
 #include "jolt_internal.h"
 
-namespace jolt {
-void make_rotation(uint64_t seed, int d, double *out);
-}
-
 using namespace jolt;
 
 // RoPE angles t * inv_freq are evaluated by a reduction valid below 2^20 rad
@@ -61,21 +57,8 @@ extern "C" const char *jolt_last_error(void) { return g_err.c_str(); }
 
 // ------------------------------------------------------------- helpers --
 static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
-static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-static inline float bf16_to_f32(uint16_t h) {
-  uint32_t u = (uint32_t)h << 16;
-  float f;
-  std::memcpy(&f, &u, 4);
-  return f;
-}
 
 // --------------------------------------------------------- cache handle --
-struct CellMeta {
-  int rT, rF, bits, rT_pad, rF_pad;
-  double a_s;  // bf16 caches: A stored as fp16(A * a_s)
-};
-
 struct jolt_cache {
   int n_layers = 0, n_groups = 0, H = 0, H_q = 0, d = 0, T = 0, T_pad = 0;
   bool f32 = false;
@@ -137,32 +120,6 @@ static jolt_status validate_desc(const jolt_cache_desc *d) {
   return JOLT_OK;
 }
 
-// ------------------------------------------------------- layout builder --
-// One host staging buffer mirrors the single device allocation.
-struct Staging {
-  std::vector<uint8_t> buf;
-  size_t take(size_t bytes) {
-    size_t off = buf.size();
-    buf.resize(off + align256(bytes), 0);
-    return off;
-  }
-};
-
-static float load_factor(const void *p, size_t i, bool f32) {
-  return f32 ? ((const float *)p)[i] : bf16_to_f32(((const uint16_t *)p)[i]);
-}
-static void store_factor(uint8_t *dst, size_t i, const void *src, size_t j, bool f32) {
-  if (f32)
-    ((float *)dst)[i] = ((const float *)src)[j];
-  else
-    ((uint16_t *)dst)[i] = ((const uint16_t *)src)[j];
-}
-
-static inline int canon_code(const uint8_t *row, int i, int bits) {
-  int per = 8 / bits;
-  return (row[i / per] >> ((i % per) * bits)) & ((1 << bits) - 1);
-}
-
 extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream stream,
                                        jolt_cache **out) {
   if (!out) return fail(JOLT_E_INVALID, "out is NULL");
@@ -176,7 +133,6 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
   if (!c) return fail(JOLT_E_OOM, "host allocation failed");
   const int H = desc->n_kv_heads, d = desc->head_dim, T = desc->T;
   const bool f32 = desc->factor_dtype == JOLT_F32;
-  const int fb = f32 ? 4 : 2;
   c->n_layers = desc->n_layers;
   c->n_groups = desc->n_groups;
   c->H = H;
@@ -191,156 +147,13 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
     for (int l = c->group_start[g]; l < c->group_start[g + 1]; ++l) c->layer_group[l] = g;
   const int T_pad = c->T_pad;
 
-  std::vector<double> Pi64((size_t)d * d);
-  make_rotation(desc->rotation_seed, d, Pi64.data());
-
-  Staging S;
+  Staged S;
   try {
-    size_t off_pi = S.take(sizeof(float) * d * d);
-    for (int i = 0; i < d * d; ++i) ((float *)(S.buf.data() + off_pi))[i] = (float)Pi64[i];
-    size_t off_pit = S.take(sizeof(float) * d * d);
-    for (int r = 0; r < d; ++r)
-      for (int c2 = 0; c2 < d; ++c2)
-        ((float *)(S.buf.data() + off_pit))[(size_t)c2 * d + r] = (float)Pi64[(size_t)r * d + c2];
-    // Pi in fp16 with padded rows: the MFMA kernel copies it to LDS as it is
-    const int pik_row = d + kRowPad;
-    size_t off_pik = S.take(sizeof(_Float16) * d * pik_row);
-    for (int r = 0; r < d; ++r)
-      for (int c2 = 0; c2 < d; ++c2)
-        ((_Float16 *)(S.buf.data() + off_pik))[(size_t)r * pik_row + c2] = (_Float16)Pi64[(size_t)r * d + c2];
-
-    struct Offs {
-      size_t A, B, Bt;
-      std::vector<size_t> G, W2, codes, scales;  // per layer in group
-    };
-    std::vector<Offs> offs(2 * c->n_groups);
-    c->cells.resize(2 * c->n_groups);
-    for (int g = 0; g < c->n_groups; ++g) {
-      const int gs = c->group_start[g + 1] - c->group_start[g];
-      for (int tau = 0; tau < 2; ++tau) {
-        const jolt_cell &in = desc->cells[2 * g + tau];
-        CellMeta m;
-        m.rT = in.r_T;
-        m.rF = in.r_F;
-        m.bits = in.bits;
-        // ranks above 256 pad to 64, so wide key tiles take an even number of
-        // 32-rank MFMA steps (fewer kernel instantiations)
-        m.rT_pad = round_up(in.r_T, in.r_T > 8 * kRankPad ? 2 * kRankPad : kRankPad);
-        m.rF_pad = round_up(in.r_F, kRankPad);
-        c->cells[2 * g + tau] = m;
-        Offs &o = offs[2 * g + tau];
-        // A.  bf16 caches: fp16 scaled by a power of two a_s (exact for every
-        // bf16 value in fp16's normal range) so that the MFMA products take A
-        // as it is -- A_K rows in the key tile, A_V against fp16 softmax
-        // weights (11-bit, where bf16 weights would carry 8); W2 carries the
-        // 1 / a_s.
-        o.A = S.take((size_t)fb * T_pad * std::max(m.rT_pad, 1));
-        m.a_s = 1.0;
-        const bool a16 = !f32;
-        if (a16) {
-          float amax = 0.0f;
-          for (size_t i = 0; i < (size_t)T * m.rT; ++i)
-            amax = std::max(amax, std::fabs(load_factor(in.A, i, false)));
-          if (amax > 0.0f) {
-            int E;
-            std::frexp(amax, &E);  // amax in [2^(E-1), 2^E)
-            m.a_s = std::ldexp(1.0, 8 - E);
-          }
-        }
-        for (int t = 0; t < T; ++t)
-          for (int r = 0; r < m.rT; ++r) {
-            size_t dst = tau == 0 ? (size_t)t * m.rT_pad + r : av_index(t, r, m.rT_pad);
-            if (a16)
-              ((_Float16 *)(S.buf.data() + o.A))[dst] =
-                  (_Float16)(load_factor(in.A, (size_t)t * m.rT + r, false) * (float)m.a_s);
-            else
-              store_factor(S.buf.data() + o.A, dst, in.A, (size_t)t * m.rT + r, f32);
-          }
-        c->cells[2 * g + tau].a_s = m.a_s;
-        // B
-        o.B = S.take((size_t)fb * d * std::max(m.rF_pad, 1));
-        for (int f = 0; f < d; ++f)
-          for (int j = 0; j < m.rF; ++j)
-            store_factor(S.buf.data() + o.B, (size_t)f * m.rF_pad + j, in.B, (size_t)f * m.rF + j,
-                         f32);
-        // B^T in float32 for the value finalize
-        o.Bt = S.take(sizeof(float) * std::max(m.rF_pad, 1) * d);
-        for (int f = 0; f < d; ++f)
-          for (int j = 0; j < m.rF; ++j)
-            ((float *)(S.buf.data() + o.Bt))[(size_t)j * d + f] =
-                load_factor(in.B, (size_t)f * m.rF + j, f32);
-        // G and residual, per layer of the group
-        for (int lp = 0; lp < gs; ++lp) {
-          size_t og = S.take((size_t)fb * H * std::max(m.rT_pad, 1) * std::max(m.rF_pad, 1));
-          o.G.push_back(og);
-          for (int h = 0; h < H; ++h)
-            for (int r = 0; r < m.rT; ++r)
-              for (int j = 0; j < m.rF; ++j) {
-                size_t src = (((size_t)lp * H + h) * m.rT + r) * m.rF + j;
-                size_t dst = tau == 0 ? ((size_t)h * m.rF_pad + j) * m.rT_pad + r
-                                      : ((size_t)h * m.rT_pad + r) * m.rF_pad + j;
-                store_factor(S.buf.data() + og, dst, in.G, src, f32);
-              }
-          // W2[h] = B G[lp, h]^T (bf16 caches): key-tile matrix (divided by
-          // a_s, the scale of the fp16 A_K) and value-finalize matrix, fp16,
-          // formed in float64 and rounded once
-          if (!f32 && m.rT > 0) {
-            // key rows padded like their LDS image
-            const int w2_row = m.rT_pad + (tau == 0 ? kRowPad : 0);
-            size_t ow = S.take(sizeof(uint16_t) * H * d * w2_row);
-            o.W2.push_back(ow);
-            _Float16 *W2 = (_Float16 *)(S.buf.data() + ow);
-            std::vector<double> Bf((size_t)d * m.rF), Gf((size_t)m.rT * m.rF);
-            for (size_t i = 0; i < Bf.size(); ++i) Bf[i] = load_factor(in.B, i, false);
-            for (int hh = 0; hh < H; ++hh) {
-              for (size_t i = 0; i < Gf.size(); ++i)
-                Gf[i] = load_factor(in.G, ((size_t)lp * H + hh) * m.rT * m.rF + i, false);
-              for (int f = 0; f < d; ++f)
-                for (int col = 0; col < m.rT_pad; ++col) {
-                  const int r = col;
-                  double acc = 0.0;
-                  if (r < m.rT)
-                    for (int j = 0; j < m.rF; ++j) acc += Bf[(size_t)f * m.rF + j] * Gf[(size_t)r * m.rF + j];
-                  W2[((size_t)hh * d + f) * w2_row + col] = (_Float16)(acc / m.a_s);
-                }
-            }
-          } else {
-            o.W2.push_back(0);
-          }
-          if (m.bits == 0) {
-            o.codes.push_back(0);
-            o.scales.push_back(0);
-            continue;
-          }
-          const int b = m.bits, rowb = d * b / 8;
-          size_t oc = S.take((size_t)H * T_pad * rowb);
-          size_t os = S.take(sizeof(float) * H * T_pad);
-          o.codes.push_back(oc);
-          o.scales.push_back(os);
-          uint8_t *C = S.buf.data() + oc;
-          float *Sc = (float *)(S.buf.data() + os);
-          for (int h = 0; h < H; ++h)
-            for (int t = 0; t < T; ++t) {
-              const uint8_t *row = in.codes + (((size_t)lp * H + h) * T + t) * rowb;
-              Sc[(size_t)h * T_pad + t] = in.scales[((size_t)lp * H + h) * T + t];
-              for (int i = 0; i < d; ++i) {
-                uint32_t code = (uint32_t)canon_code(row, i, b);
-                int dw, sh;
-                if (tau == 0) {
-                  int s = i >> 5, g2 = (i >> 3) & 3, j = i & 7;
-                  code_pos(8 * s + j, b, &dw, &sh);
-                  uint32_t *w = (uint32_t *)(C + ((size_t)h * T_pad + t) * rowb + g2 * (d * b / 32));
-                  w[dw] |= code << sh;
-                } else {
-                  size_t at;
-                  vcode_pos(h, t, i, b, T_pad, d, &at, &sh);
-                  *(uint32_t *)(C + at) |= code << sh;
-                }
-              }
-            }
-        }
-      }
-    }
+    // host image of the device layout (layout.cpp): Pi from the seed, the
+    // factors, W2 = B G^T and the re-packed codes
+    stage_cache(desc, &S);
+    c->cells = S.cells;
+    const std::vector<CellOffsets> &offs = S.offs;
     size_t off_layers = S.take(sizeof(LayerDev) * c->n_layers);
     c->dev_bytes = S.buf.size();
     hipError_t e = hipMalloc(&c->dev, c->dev_bytes);
@@ -349,22 +162,22 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
       return fail(e == hipErrorOutOfMemory ? JOLT_E_OOM : JOLT_E_HIP, "hipMalloc(%zu): %s",
                   S.buf.size(), hipGetErrorString(e));
     }
-    hipGetDevice(&c->device);
+    (void)hipGetDevice(&c->device);
     uint8_t *base = (uint8_t *)c->dev;
     c->h_layers.resize(c->n_layers);
     for (int l = 0; l < c->n_layers; ++l) {
       const int g = c->layer_group[l], lp = l - c->group_start[g];
       LayerDev &L = c->h_layers[l];
       std::memset(&L, 0, sizeof L);
-      L.Pi = (const float *)(base + off_pi);
-      L.PiT = (const float *)(base + off_pit);
-      L.PiK = (const _Float16 *)(base + off_pik);
+      L.Pi = (const float *)(base + S.off_pi);
+      L.PiT = (const float *)(base + S.off_pit);
+      L.PiK = (const _Float16 *)(base + S.off_pik);
       L.T = T;
       L.T_pad = T_pad;
       L.f32 = f32 ? 1 : 0;
       for (int tau = 0; tau < 2; ++tau) {
         const CellMeta &m = c->cells[2 * g + tau];
-        const Offs &o = offs[2 * g + tau];
+        const CellOffsets &o = offs[2 * g + tau];
         CellDev &cd = L.c[tau];
         cd.A = base + o.A;
         cd.B = base + o.B;
@@ -387,12 +200,12 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
     e = hipMemcpyAsync(c->dev, S.buf.data(), S.buf.size(), hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) {
-      hipFree(c->dev);
+      (void)hipFree(c->dev);
       delete c;
       return fail(JOLT_E_HIP, "upload: %s", hipGetErrorString(e));
     }
   } catch (const std::bad_alloc &) {
-    if (c->dev) hipFree(c->dev);
+    if (c->dev) (void)hipFree(c->dev);
     delete c;
     return fail(JOLT_E_OOM, "host staging allocation failed");
   }
@@ -503,6 +316,8 @@ static jolt_status plan_decode(const jolt_cache *const *caches, int batch, int l
   if (want < 0 || want > 2) return fail(JOLT_E_INVALID, "launch->kernel=%d", want);
   if (launch && launch->split_tokens < 0)
     return fail(JOLT_E_INVALID, "launch->split_tokens=%d", launch->split_tokens);
+  if (launch && launch->deterministic != 0 && launch->deterministic != 1)
+    return fail(JOLT_E_INVALID, "launch->deterministic=%d", launch->deterministic);
   p->T_max = 1;
   p->rV_max = 0;
   bool mf = batch > 0;
@@ -627,6 +442,7 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
       ma.split_tokens = a.split_tokens;
       ma.stride = a.stride;
       ma.grid8 = (a.n_split & 7) == 0;
+      ma.fixed_blocks = launch && launch->deterministic ? 1 : 0;
       bool done[kMaxBatchPerLaunch] = {};
       int last_class = 0;  // first member of the chunk's last launch class
       for (int i0 = 0; i0 < nb; ++i0) {

@@ -1,82 +1,24 @@
 // Internal types shared by the host code and the HIP kernels of libjolt.
 //
 // Device layout of a loaded cache (private; chosen for gfx950 MFMA operand
-// fragments, see the comments on each field).  Notation: H KV heads, d head
-// dim, T tokens, T_pad = T rounded up to 128, ranks padded to multiples of 32
-// with zeros (a zero rank column contributes nothing to any product).
+// fragments, see the comments on each field and layout.h for the index
+// maps).  Notation: H KV heads, d head dim, T tokens, T_pad = T rounded up to
+// 128, ranks padded to multiples of 32 with zeros.
 #pragma once
 #include <stdint.h>
 
 #include <hip/hip_runtime.h>
 
 #include "jolt.h"
+#include "layout.h"  // constants and index maps of the device layout
 
 namespace jolt {
 
-constexpr int kTokPad = 128;    // T padding: one MFMA workgroup tile
-constexpr int kRankPad = 32;    // rank padding: one 16x16x32 MFMA K-step
-// fp16 elements appended to each row of the key-tile matrices (W2_K, Pi),
-// which are copied to LDS as they are.  With rows of 64 k + 32 bytes the
-// MFMA operand reads (lane (r, g): row r, 16-byte chunk g) reach the full
-// LDS rate on gfx950; strides of 64 k + 16 or 64 k + 48 bytes run at ~57 %
-// of it, multiples of 64 far lower (measured with ds_read_b128).
-constexpr int kRowPad = 16;
 constexpr int kMaxHg = 16;      // query heads per KV head
 constexpr int kMaxBatchPerLaunch = 32;
 constexpr int kMaxD = 128;
 constexpr int kMaxSplits = 2048;
 constexpr double kRopeSmall = 128.0;  // radians; see MfmaArgs::rope_small
-
-// Slot order of a 32-deep MFMA K step built from two 16x16 result tiles:
-// slot q = 8g + j (g = 16-lane group, j = element of the 8-wide operand)
-// holds row perm32(q) of the pair of tiles (lane group g holds rows
-// 4g..4g+3 of each).  The key path feeds its rebuilt feature rows to the
-// score product in this order, and the queries are laid out to match.
-__host__ __device__ inline int perm32(int q) {
-  int g = q >> 3, j = q & 7;
-  return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
-}
-__host__ __device__ inline int perm32_inv(int t) {
-  if (t < 16) return 8 * (t >> 2) + (t & 3);
-  t -= 16;
-  return 8 * (t >> 2) + 4 + (t & 3);
-}
-
-// Packed-code position of slot q (0..31 within one 32-slot group) for b bits:
-// dword q/2/(16/b), bit offset b*((q/2)%(16/b) + (q&1)*(16/b)).  With this
-// order one shift and one mask by (2^b-1)|(2^b-1)<<16 place two consecutive
-// slots in the two halves of a 32-bit word (two fp16 lanes).
-__host__ __device__ inline void code_pos(int q, int bits, int *dword, int *shift) {
-  int npair = 16 / bits;
-  int P = q >> 1;
-  *dword = P / npair;
-  *shift = bits * ((P % npair) + (q & 1) * npair);
-}
-
-// Value-side layouts follow the operands of a 16x16x16 MFMA whose K
-// dimension is 16 tokens: lane (row & 15) * 4 + (t & 15) / 4 holds the four
-// consecutive tokens t & ~3 .. (t & ~3) + 3 of one row (a value rank or a
-// rotated feature), so a score tile (lane group g holds tokens 4g..4g+3 of
-// one query) is the other operand as it stands.
-//
-// A_V element (t, r): 16 x 16 tiles per (16-token block, 16-rank block).
-__host__ __device__ inline size_t av_index(int t, int r, int rT_pad) {
-  return (((size_t)(t >> 4) * (rT_pad >> 4) + (r >> 4)) * 64 + (r & 15) * 4 + ((t & 15) >> 2)) * 4 +
-         (t & 3);
-}
-// Value code of (head h, token t, rotated feature f) for b bits and head
-// dim d: per (head, 16-token block) 64 lane records of d*b/32 bytes; the
-// record of lane (f & 15) * 4 + (t & 15) / 4 holds the d/4 slots
-// q = 4 (f / 16) + (t & 3) in code_pos order.  Returns the byte offset of the
-// slot's 32-bit word and the bit offset inside it.
-__host__ __device__ inline void vcode_pos(int h, int t, int f, int bits, int T_pad, int d,
-                                          size_t *byte, int *shift) {
-  int dw, sh;
-  code_pos(4 * (f >> 4) + (t & 3), bits, &dw, &sh);
-  const size_t lane = (size_t)(f & 15) * 4 + ((t & 15) >> 2);
-  *byte = (((size_t)h * (T_pad >> 4) + (t >> 4)) * 64 + lane) * (size_t)(d * bits / 32) + 4 * dw;
-  *shift = sh;
-}
 
 struct CellDev {
   // K: A [T_pad][rT_pad] row-major (fp16, scaled, for bf16 caches).
@@ -159,6 +101,9 @@ struct MfmaArgs {
   // bit m: every angle t * inv_freq[f] of the launch with 16 m <= f < 16 m + 16
   // is at most kRopeSmall radians (such blocks skip the 2 pi reduction)
   int32_t rope_small;
+  // 1: fixed token-block schedule (wave w takes blocks w, w + waves, ...),
+  // bitwise reproducible; 0: blocks claimed on demand
+  int32_t fixed_blocks;
   SeqMfma seq[kMaxBatchPerLaunch];
 };
 static_assert(sizeof(MfmaArgs) <= 4096, "MFMA kernel arguments exceed 4 KiB");

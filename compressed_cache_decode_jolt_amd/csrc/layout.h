@@ -1,0 +1,144 @@
+// Device layout of a loaded cache: index maps and the host-side staging of
+// one cache's device image.  Plain C++ (no HIP runtime), so the re-layout can
+// be built and checked on a CPU alone, under the address and undefined-
+// behaviour sanitizers; the kernels include the same index maps through
+// jolt_internal.h.
+//
+// Notation: H KV heads, d head dim, T tokens, T_pad = T rounded up to 128,
+// ranks padded to multiples of 32 with zeros (a zero rank column contributes
+// nothing to any product).
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "jolt.h"
+
+#if defined(__HIPCC__)
+#define JOLT_HD __host__ __device__
+#else
+#define JOLT_HD
+#endif
+
+namespace jolt {
+
+constexpr int kTokPad = 128;    // T padding: one MFMA workgroup tile
+constexpr int kRankPad = 32;    // rank padding: one 16x16x32 MFMA K-step
+// fp16 elements appended to each row of the key-tile matrices (W2_K, Pi),
+// which are copied to LDS as they are.  With rows of 64 k + 32 bytes the
+// MFMA operand reads (lane (r, g): row r, 16-byte chunk g) reach the full
+// LDS rate on gfx950; strides of 64 k + 16 or 64 k + 48 bytes run at ~57 %
+// of it, multiples of 64 far lower (measured with ds_read_b128).
+constexpr int kRowPad = 16;
+
+// Slot order of a 32-deep MFMA K step built from two 16x16 result tiles:
+// slot q = 8g + j (g = 16-lane group, j = element of the 8-wide operand)
+// holds row perm32(q) of the pair of tiles (lane group g holds rows
+// 4g..4g+3 of each).  The key path feeds its rebuilt feature rows to the
+// score product in this order, and the queries are laid out to match.
+JOLT_HD inline int perm32(int q) {
+  int g = q >> 3, j = q & 7;
+  return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
+}
+JOLT_HD inline int perm32_inv(int t) {
+  if (t < 16) return 8 * (t >> 2) + (t & 3);
+  t -= 16;
+  return 8 * (t >> 2) + 4 + (t & 3);
+}
+
+// Packed-code position of slot q (0..31 within one 32-slot group) for b bits:
+// dword q/2/(16/b), bit offset b*((q/2)%(16/b) + (q&1)*(16/b)).  With this
+// order one shift and one mask by (2^b-1)|(2^b-1)<<16 place two consecutive
+// slots in the two halves of a 32-bit word (two fp16 lanes).
+JOLT_HD inline void code_pos(int q, int bits, int *dword, int *shift) {
+  int npair = 16 / bits;
+  int P = q >> 1;
+  *dword = P / npair;
+  *shift = bits * ((P % npair) + (q & 1) * npair);
+}
+
+// Key residual codes: a row of one (head, token) is d*b/8 bytes in 4 chunks
+// of d*b/32 bytes, one per 16-lane group g of the MFMA operand; chunk g holds
+// rotated feature i = 32 s + 8 g + j as slot q = 8 s + j in code_pos order.
+JOLT_HD inline void kcode_pos(int h, int t, int i, int bits, int T_pad, int d, size_t *byte,
+                              int *shift) {
+  int dw, sh;
+  code_pos(8 * (i >> 5) + (i & 7), bits, &dw, &sh);
+  *byte = ((size_t)h * T_pad + t) * (size_t)(d * bits / 8) + ((i >> 3) & 3) * (size_t)(d * bits / 32) +
+          4 * (size_t)dw;
+  *shift = sh;
+}
+
+// Value-side layouts follow the operands of a 16x16x16 MFMA whose K
+// dimension is 16 tokens: lane (row & 15) * 4 + (t & 15) / 4 holds the four
+// consecutive tokens t & ~3 .. (t & ~3) + 3 of one row (a value rank or a
+// rotated feature), so a score tile (lane group g holds tokens 4g..4g+3 of
+// one query) is the other operand as it stands.
+//
+// A_V element (t, r): 16 x 16 tiles per (16-token block, 16-rank block).
+JOLT_HD inline size_t av_index(int t, int r, int rT_pad) {
+  return (((size_t)(t >> 4) * (rT_pad >> 4) + (r >> 4)) * 64 + (r & 15) * 4 + ((t & 15) >> 2)) * 4 +
+         (t & 3);
+}
+// Value code of (head h, token t, rotated feature f) for b bits and head
+// dim d: per (head, 16-token block) 64 lane records of d*b/32 bytes; the
+// record of lane (f & 15) * 4 + (t & 15) / 4 holds the d/4 slots
+// q = 4 (f / 16) + (t & 3) in code_pos order.  Returns the byte offset of the
+// slot's 32-bit word and the bit offset inside it.
+JOLT_HD inline void vcode_pos(int h, int t, int f, int bits, int T_pad, int d, size_t *byte,
+                              int *shift) {
+  int dw, sh;
+  code_pos(4 * (f >> 4) + (t & 3), bits, &dw, &sh);
+  const size_t lane = (size_t)(f & 15) * 4 + ((t & 15) >> 2);
+  *byte = (((size_t)h * (T_pad >> 4) + (t >> 4)) * 64 + lane) * (size_t)(d * bits / 32) + 4 * dw;
+  *shift = sh;
+}
+
+// Padded rank of a cell: multiples of 32; ranks above 256 pad to 64, so wide
+// key tiles take an even number of 32-rank MFMA steps.
+inline int pad_rank(int r) {
+  const int m = r > 8 * kRankPad ? 2 * kRankPad : kRankPad;
+  return (r + m - 1) / m * m;
+}
+
+struct CellMeta {
+  int rT, rF, bits, rT_pad, rF_pad;
+  double a_s;  // bf16 caches: A stored as fp16(A * a_s), a_s a power of two
+};
+
+// Byte offsets, inside one staging buffer, of a cell's sections (per layer
+// of its group where the section is per layer; 0 = absent).
+struct CellOffsets {
+  size_t A = 0, B = 0, Bt = 0;
+  std::vector<size_t> G, W2, codes, scales;
+};
+
+// The device image of one cache, built in host memory: one buffer that is
+// copied to a single device allocation as it is.  Sections start at
+// 256-byte boundaries.
+//   Pi fp32 [d][d], Pi^T fp32 [d][d], PiK fp16 [d][d + kRowPad];
+//   per cell: A -- keys [T_pad][rT_pad] (fp16 A*a_s for bf16 caches, fp32
+//   otherwise), values in the av_index layout; B [d][rF_pad] (factor dtype);
+//   B^T fp32 [rF_pad][d]; per layer: G (K: [H][rF_pad][rT_pad], V:
+//   [H][rT_pad][rF_pad]), W2 = B G[h]^T / a_s fp16 for bf16 caches (keys
+//   [H][d][rT_pad + kRowPad], values [H][d][rT_pad]), codes (K: kcode_pos,
+//   V: vcode_pos layout) and scales fp32 [H][T_pad].
+struct Staged {
+  std::vector<uint8_t> buf;
+  int T_pad = 0;
+  size_t off_pi = 0, off_pit = 0, off_pik = 0;
+  std::vector<CellMeta> cells;      // [n_groups * 2]
+  std::vector<CellOffsets> offs;    // [n_groups * 2]
+  size_t take(size_t bytes);        // append a zeroed, 256-aligned section
+};
+
+// Fill *out from a descriptor that has passed validation.  Regenerates Pi
+// from the seed, re-lays out A, B, G, W2, codes and scales.  Throws
+// std::bad_alloc when host memory runs out.  Uses up to `threads` host
+// threads (0 = all hardware threads).
+void stage_cache(const jolt_cache_desc *desc, Staged *out, int threads = 0);
+
+void make_rotation(uint64_t seed, int d, double *out);
+
+}  // namespace jolt

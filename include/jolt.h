@@ -99,6 +99,12 @@ typedef struct {
                          /* call / the end time of its last one (kernel           */
                          /* timestamps, not stream markers), so a caller can time */
                          /* the split-T kernels alone                             */
+  int32_t deterministic; /* 1: fixed assignment of token blocks to waves, so two  */
+                         /* calls with the same inputs and settings give the same */
+                         /* output bits (the Reproducibility Statement of the     */
+                         /* JoLT summary asks for repeatable results); 0: blocks  */
+                         /* handed out on demand (faster, last-bit differences    */
+                         /* between runs)                                         */
 } jolt_launch;
 
 /*

@@ -132,7 +132,9 @@ def test_llama8b_layer_workload(l8b, kernel):
     want = oracle_decode([c], 0, q, [cfg.T], inv, scale)
     r, mx = rel_l2(got, want), float(np.max(np.abs(got - want)))
     print(f"llama8b layer kernel={kernel}: rel_l2={r:.3e} max_abs={mx:.3e}")
-    assert r <= 5e-3 and mx <= 2e-2
+    # the automatic choice here is the MFMA kernel
+    rt, at = tol(J.KERNEL_MFMA if kernel is None else kernel, False)
+    assert r <= rt and mx <= at
 
 
 # ------------------------------------------------------------- coverage --
@@ -285,8 +287,9 @@ def test_two_blocks_per_step_on_short_key_chains(split):
 @pytest.mark.parametrize("split", [0, 256])
 def test_one_query_batch_of_mixed_classes(split):
     """One query per KV head, one batch whose sequences fall in different
-    launch classes (8 waves; 4 waves with value ranks above 128, two token
-    blocks per step; 4 waves with key ranks above 256) and lengths."""
+    launch classes and lengths: 8 waves (value ranks up to 64), the one-query
+    8-wave class for value ranks above 128, and the one-query 4-wave class
+    for key ranks above 256."""
     d, H, H_q = 128, 4, 4
     spec = [(300, (96, 64, 4), (64, 32, 2)), (1000, (160, 64, 8), (400, 96, 4)),
             (400, (352, 96, 2), (128, 64, 8)), (513, (96, 64, 4), (64, 32, 2))]
@@ -433,3 +436,56 @@ def test_rope_sincos_accuracy(variant, bound):
     b64 = big.astype(np.float64)
     worst = max(worst, np.max(np.abs(sn - np.sin(b64))), np.max(np.abs(cs - np.cos(b64))))
     assert worst <= bound, worst
+
+
+@pytest.mark.parametrize("split", [512, 1024])
+def test_one_query_two_blocks_per_step(split):
+    """One query per KV head on the class with two 16-token blocks per wave
+    step (key and value ranks up to 64, splits of at least 512 tokens),
+    ragged lengths whose last split is short."""
+    d, H, H_q = 128, 4, 4
+    spec = [(1111, (48, 32, 4), (64, 32, 2)), (1500, (64, 64, 8), (32, 32, 8)),
+            (700, (32, 16, 0), (16, 16, 4))]
+    caches = [gen.small_cache(160 + i, T, H, H_q, d, [(aK, aV)], [1])
+              for i, (T, aK, aV) in enumerate(spec)]
+    inv = gen.rope_inv_freq_input(1e4, d)
+    q = np.stack([gen.queries(161, i, 0, H_q, d, "bf16") for i in range(len(spec))])
+    q_pos = [T for T, _, _ in spec]
+    got = run_decode(caches, 0, q, q_pos, inv, 0.088, kernel=J.KERNEL_MFMA, split=split)
+    want = oracle_decode(caches, 0, q, q_pos, inv, 0.088)
+    for b in range(len(spec)):
+        assert rel_l2(got[b], want[b]) <= 5e-3, (b, rel_l2(got[b], want[b]))
+        assert np.max(np.abs(got[b] - want[b])) <= 2e-2
+
+
+DET_CASES = [(2, 8, 1500, (64, 32, 4), (48, 32, 2), 512),     # 8 waves, two blocks per step
+             (2, 8, 2000, (96, 64, 8), (96, 64, 4), 0),       # 8 waves, value ranks <= 128
+             (4, 4, 1300, (320, 64, 2), (160, 64, 8), 256),   # one query, wide keys, 4 waves
+             (4, 4, 1300, (160, 64, 4), (400, 96, 4), 0),     # one query, value ranks > 128
+             (2, 16, 900, (128, 64, 0), (256, 64, 2), 0)]     # 4 waves, value ranks > 128
+
+
+@pytest.mark.parametrize("H,H_q,T,aK,aV,split", DET_CASES,
+                         ids=["nb2", "v128", "hg1-widek", "hg1-widev", "wide-v"])
+def test_deterministic_schedule_is_bitwise_repeatable(H, H_q, T, aK, aV, split):
+    """With the fixed block schedule, repeated calls give identical output
+    bytes (and stay within the tolerance of the oracle)."""
+    d = 128
+    c = gen.small_cache(170 + H + aK[0] // 16, T, H, H_q, d, [(aK, aV)], [1])
+    inv = gen.rope_inv_freq_input(5e5, d)
+    q = gen.queries(171, H, aK[0], H_q, d, "bf16")[None]
+    h = J.jolt_load_cache(c)
+    qt = torch.from_numpy(q).to(torch.bfloat16).cuda()
+    nb = J.jolt_decode_workspace_size([h], 0, split_tokens=split)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(4):
+        out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+        J.jolt_decode_attention([h], 0, qt, [T], inv, 0.088, out, ws, split_tokens=split,
+                                deterministic=True)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+    want = oracle_decode([c], 0, q, [T], inv, 0.088)
+    assert rel_l2(outs[0].astype(np.float64), want) <= 5e-3
