@@ -8,6 +8,7 @@ functions; they keep the C names.
 from ._jolt import (  # noqa: F401
     Cache, JoltError, KERNEL_AUTO, KERNEL_GENERIC, KERNEL_MFMA, LIB_PATH, EXPORTS,
     jolt_load_cache, jolt_decode_workspace_size, jolt_decode_attention,
+    jolt_decode_tail_workspace_size, jolt_decode_attention_tail,
     jolt_dense_workspace_size, jolt_dense_attention, jolt_make_rotation, jolt_debug_unpack, jolt_debug_sincos,
     jolt_last_error, lib,
 )

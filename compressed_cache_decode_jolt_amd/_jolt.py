@@ -55,6 +55,15 @@ EXPORTS = {
                                         C.c_int, C.POINTER(C.c_int32), C.POINTER(C.c_float),
                                         C.c_float, C.c_void_p, C.c_void_p, C.c_size_t,
                                         C.POINTER(jolt_launch), C.c_void_p]),
+    "jolt_decode_tail_workspace_size": (C.c_int, [C.POINTER(C.c_void_p), C.c_int32, C.c_int32,
+                                                  C.c_int32, C.POINTER(jolt_launch),
+                                                  C.POINTER(C.c_size_t)]),
+    "jolt_decode_attention_tail": (C.c_int, [C.POINTER(C.c_void_p), C.c_int32, C.c_int32,
+                                             C.c_void_p, C.c_int, C.POINTER(C.c_int32),
+                                             C.POINTER(C.c_float), C.c_float, C.c_void_p,
+                                             C.c_void_p, C.c_int, C.c_int32,
+                                             C.POINTER(C.c_int32), C.c_void_p, C.c_void_p,
+                                             C.c_size_t, C.POINTER(jolt_launch), C.c_void_p]),
     "jolt_dense_workspace_size": (C.c_int, [C.c_int32] * 5 + [C.POINTER(jolt_launch),
                                                               C.POINTER(C.c_size_t)]),
     "jolt_dense_attention": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int] + [C.c_int32] * 5 +
@@ -270,6 +279,45 @@ def jolt_decode_attention(caches, layer, q, q_pos, inv_freq, softmax_scale, out,
         inv.ctypes.data_as(C.POINTER(C.c_float)), C.c_float(softmax_scale), _ptr(out),
         _ptr(_workspace(workspace)), _nbytes(workspace), C.byref(L) if L else None,
         _stream(stream)))
+
+
+def jolt_decode_tail_workspace_size(caches, layer, tail_cap, kernel=None, split_tokens=0):
+    n = C.c_size_t()
+    L = _launch(kernel, split_tokens)
+    _check(lib().jolt_decode_tail_workspace_size(_handles(caches), len(caches), layer,
+                                                 int(tail_cap), C.byref(L) if L else None,
+                                                 C.byref(n)))
+    return n.value
+
+
+def jolt_decode_attention_tail(caches, layer, q, q_pos, inv_freq, softmax_scale, k_tail, v_tail,
+                               tail_len, out, workspace, kernel=None, split_tokens=0,
+                               stream=None, deterministic=False):
+    """As jolt_decode_attention, plus an uncompressed tail: k_tail / v_tail
+    device [B, H, tail_cap, d] (f32/bf16, keys already rotated to their
+    positions), tail_len [B] valid rows per sequence."""
+    import torch
+    B = len(caches)
+    if B == 0:
+        return
+    m = caches[0].meta
+    shape = (B, m["H_q"], m["d"])
+    _check_tensor("q", q, (torch.float32, torch.bfloat16), shape)
+    _check_tensor("out", out, (torch.float32,), shape)
+    cap = k_tail.shape[2]
+    _check_tensor("k_tail", k_tail, (torch.float32, torch.bfloat16), (B, m["H"], cap, m["d"]))
+    _check_tensor("v_tail", v_tail, (k_tail.dtype,), (B, m["H"], cap, m["d"]))
+    if len(q_pos) != B or len(tail_len) != B:
+        raise ValueError("q_pos and tail_len need one entry per sequence")
+    inv = _inv_freq(inv_freq, m["d"])
+    qp = (C.c_int32 * B)(*[int(x) for x in q_pos])
+    tl = (C.c_int32 * B)(*[int(x) for x in tail_len])
+    L = _launch(kernel, split_tokens, None, deterministic)
+    _check(lib().jolt_decode_attention_tail(
+        _handles(caches), B, layer, _ptr(q), _dtype_code(q), qp,
+        inv.ctypes.data_as(C.POINTER(C.c_float)), C.c_float(softmax_scale), _ptr(k_tail),
+        _ptr(v_tail), _dtype_code(k_tail), int(cap), tl, _ptr(out), _ptr(_workspace(workspace)),
+        _nbytes(workspace), C.byref(L) if L else None, _stream(stream)))
 
 
 def jolt_dense_workspace_size(batch, n_kv, n_q, d, T, kernel=None, split_tokens=0):

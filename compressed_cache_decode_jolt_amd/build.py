@@ -6,6 +6,7 @@ Objects go to _build/ at the repository root; the shared library is written
 next to this file so that it travels with the source tree.
 """
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -43,14 +44,40 @@ def sources():
                   if f.endswith((".cpp", ".hip")))
 
 
+def scratch_users(remarks):
+    """Kernels of the compiler's resource-usage remarks that use scratch
+    (register spills): {kernel name: bytes per lane}."""
+    out, name = {}, None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and int(m.group(1)) > 0:
+            out[name] = int(m.group(1))
+    return out
+
+
 def compile_one(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [hipcc(), *COMMON, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
+    # The MFMA decode instantiations must not spill: every launch class is
+    # sized to its registers, and spill code of this compiler once dropped a
+    # reloaded operand in one of them (silently wrong results).
+    decode = os.path.basename(src).startswith("mfma_k")
+    if decode:
+        cmd.append("-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if decode:
+        bad = {k: v for k, v in scratch_users(r.stderr).items() if "decode_mfma" in k}
+        if bad:
+            raise RuntimeError(f"{os.path.basename(src)}: decode kernels use scratch (register "
+                               f"spills): {bad}")
     return obj
 
 

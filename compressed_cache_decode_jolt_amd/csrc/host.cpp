@@ -237,6 +237,12 @@ extern "C" jolt_status jolt_cache_info(const jolt_cache *c, int32_t *n_layers, i
 struct Plan {
   int kernel;        // JOLT_KERNEL_GENERIC or JOLT_KERNEL_MFMA
   int split_tokens, n_split, rV_max, stride, T_max;
+  // uncompressed tail: splits of tail_split tokens over tail_cap rows; the
+  // MFMA path keeps their partials in the same rows as the split kernel's
+  // (splits n_split .. n_split + n_tsplit - 1), the float32 path in a region
+  // of its own at byte tail_off of the workspace
+  int tail_split, n_tsplit;
+  size_t tail_off;
   size_t ws_bytes;
 };
 
@@ -256,7 +262,8 @@ static int mfma_lds_bytes(const CellDev &k, const CellDev &v, int d, bool hg1) {
   const bool wide = k.rT_pad > 8 * kRankPad;
   const int kpath = 2 * d * (k.rT_pad + kRowPad) + (k.bits > 0 && !wide ? 2 * d * (d + kRowPad) : 0);
   const bool big_v = v.rT_pad / 16 > 8;
-  const bool hg1v = hg1 && (wide || big_v);  // launched as an HG1 variant
+  // launched as an HG1 variant
+  const bool hg1v = hg1 && hg1_variant(k.bits, v.bits, k.rT_pad / kRankPad, v.rT_pad / 16);
   const int waves = wide || (big_v && !hg1v) ? 4 : 8;
   // fp16 value partials of every wave
   const int park = waves * (v.rT_pad / 16 + 8) * (hg1v ? 32 : 512);
@@ -271,6 +278,10 @@ static bool mfma_ok(const jolt_cache *c, int layer, int *lds) {
   const CellDev &k = L.c[0], &v = L.c[1];
   if (v.rT_pad > 512 || k.rT_pad > 512) return false;
   if (k.rT_pad > 8 * kRankPad && v.rT_pad > 256) return false;  // no such class
+  // key ranks above 256 with value ranks above 128 run on MFMA only with one
+  // query per KV head (the grouped-query variant would need more registers
+  // than a SIMD has; see mfma_launch.inc)
+  if (k.rT_pad > 8 * kRankPad && v.rT_pad > 128 && c->H_q != c->H) return false;
   *lds = mfma_lds_bytes(k, v, c->d, c->H_q == c->H);
   return *lds <= jolt_mfma_max_lds();
 }
@@ -298,7 +309,7 @@ static int cu_count() {
 }
 
 static jolt_status plan_decode(const jolt_cache *const *caches, int batch, int layer,
-                               const jolt_launch *launch, Plan *p) {
+                               const jolt_launch *launch, int tail_cap, Plan *p) {
   if (batch < 0) return fail(JOLT_E_INVALID, "batch=%d", batch);
   if (batch > 0 && !caches) return fail(JOLT_E_INVALID, "caches is NULL");
   const jolt_cache *c0 = batch ? caches[0] : nullptr;
@@ -364,7 +375,24 @@ static jolt_status plan_decode(const jolt_cache *const *caches, int batch, int l
   p->n_split = (p->T_max + p->split_tokens - 1) / p->split_tokens;
   p->stride = p->kernel == JOLT_KERNEL_MFMA ? 4 + (batch ? c0->d : 0)
                                             : partial_stride(p->rV_max, batch ? c0->d : 0);
-  p->ws_bytes = (size_t)batch * (batch ? c0->H_q : 0) * p->n_split * p->stride * sizeof(float);
+  // tail splits: about one workgroup round over the batch's KV heads
+  p->tail_split = p->n_tsplit = 0;
+  if (tail_cap > 0) {
+    const int n = std::max(1, (cu_count() + batch * H - 1) / std::max(1, batch * H));
+    int ts = round_up(std::max(1, (tail_cap + n - 1) / n), 64);
+    ts = std::max(ts, round_up((tail_cap + kMaxTailSplits - 1) / kMaxTailSplits, 64));
+    p->tail_split = ts;
+    p->n_tsplit = (tail_cap + ts - 1) / ts;
+  }
+  const size_t rows = (size_t)batch * (batch ? c0->H_q : 0);
+  const int dd = batch ? c0->d : 0;
+  if (p->kernel == JOLT_KERNEL_MFMA) {
+    p->tail_off = 0;
+    p->ws_bytes = rows * (p->n_split + p->n_tsplit) * p->stride * sizeof(float);
+  } else {
+    p->tail_off = rows * p->n_split * p->stride * sizeof(float);
+    p->ws_bytes = p->tail_off + rows * p->n_tsplit * (4 + dd) * sizeof(float);
+  }
   return JOLT_OK;
 }
 
@@ -373,20 +401,40 @@ extern "C" jolt_status jolt_decode_workspace_size(const jolt_cache *const *cache
                                                   size_t *bytes) {
   if (!bytes) return fail(JOLT_E_INVALID, "bytes is NULL");
   Plan p;
-  jolt_status st = plan_decode(caches, batch, layer, launch, &p);
+  jolt_status st = plan_decode(caches, batch, layer, launch, 0, &p);
   if (st != JOLT_OK) return st;
   *bytes = p.ws_bytes;
   return ok();
 }
 
-extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, int32_t batch,
-                                             int32_t layer, const void *q, jolt_dtype q_dtype,
-                                             const int32_t *q_pos, const float *inv_freq,
-                                             float softmax_scale, float *out, void *workspace,
-                                             size_t ws_bytes, const jolt_launch *launch,
-                                             jolt_stream stream) {
+extern "C" jolt_status jolt_decode_tail_workspace_size(const jolt_cache *const *caches,
+                                                       int32_t batch, int32_t layer,
+                                                       int32_t tail_cap,
+                                                       const jolt_launch *launch, size_t *bytes) {
+  if (!bytes) return fail(JOLT_E_INVALID, "bytes is NULL");
+  if (tail_cap < 0 || tail_cap > kMaxPos) return fail(JOLT_E_INVALID, "tail_cap=%d", tail_cap);
   Plan p;
-  jolt_status st = plan_decode(caches, batch, layer, launch, &p);
+  jolt_status st = plan_decode(caches, batch, layer, launch, tail_cap, &p);
+  if (st != JOLT_OK) return st;
+  *bytes = p.ws_bytes;
+  return ok();
+}
+
+// An uncompressed tail of post-RoPE keys and values (see jolt.h).
+struct TailIn {
+  const void *k = nullptr, *v = nullptr;
+  jolt_dtype dtype = JOLT_BF16;
+  int cap = 0;
+  const int32_t *len = nullptr;
+};
+
+static jolt_status decode_impl(const jolt_cache *const *caches, int32_t batch, int32_t layer,
+                               const void *q, jolt_dtype q_dtype, const int32_t *q_pos,
+                               const float *inv_freq, float softmax_scale, const TailIn &tail,
+                               float *out, void *workspace, size_t ws_bytes,
+                               const jolt_launch *launch, jolt_stream stream) {
+  Plan p;
+  jolt_status st = plan_decode(caches, batch, layer, launch, tail.cap, &p);
   if (st != JOLT_OK) return st;
   if (batch == 0) return ok();
   if (!q || !q_pos || !inv_freq || !out) return fail(JOLT_E_INVALID, "NULL q/q_pos/inv_freq/out");
@@ -394,6 +442,13 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
   if (!std::isfinite(softmax_scale)) return fail(JOLT_E_INVALID, "softmax_scale not finite");
   if (check_rope(q_pos, batch, inv_freq, caches[0]->d) != JOLT_OK)
     return fail(JOLT_E_INVALID, "q_pos must lie in [0, 2^20] and inv_freq in [0, 1]");
+  if (tail.cap > 0) {
+    if (!tail.k || !tail.v || !tail.len) return fail(JOLT_E_INVALID, "NULL tail pointer");
+    if (tail.dtype != JOLT_F32 && tail.dtype != JOLT_BF16) return fail(JOLT_E_INVALID, "tail dtype");
+    for (int b = 0; b < batch; ++b)
+      if (tail.len[b] < 0 || tail.len[b] > tail.cap)
+        return fail(JOLT_E_INVALID, "tail_len[%d]=%d outside [0, %d]", b, tail.len[b], tail.cap);
+  }
   if (!workspace || ws_bytes < p.ws_bytes)
     return fail(JOLT_E_WORKSPACE, "workspace %zu bytes, need %zu", workspace ? ws_bytes : 0,
                 p.ws_bytes);
@@ -414,11 +469,19 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
   a.stride = p.stride;
   a.rV_max = p.rV_max;
   const size_t qbytes = (size_t)c0->H_q * c0->d * (a.q_f32 ? 4 : 2);
+  const bool mfma = p.kernel == JOLT_KERNEL_MFMA;
+  // splits per workspace row: the MFMA path keeps the tail's partials in the
+  // same rows, after the split kernel's
+  const int ws_splits = mfma ? p.n_split + p.n_tsplit : p.n_split;
   for (int b0 = 0; b0 < batch; b0 += kMaxBatchPerLaunch) {
     int nb = std::min(kMaxBatchPerLaunch, batch - b0);
     a.q = (const uint8_t *)q + b0 * qbytes;
     a.out = out + (size_t)b0 * c0->H_q * c0->d;
-    a.ws = (float *)workspace + (size_t)b0 * c0->H_q * p.n_split * p.stride;
+    a.ws = (float *)workspace + (size_t)b0 * c0->H_q * ws_splits * p.stride;
+    a.n_tsplit = mfma ? 0 : p.n_tsplit;
+    a.tail_ws = mfma || !p.n_tsplit ? nullptr
+                                    : (const float *)((const uint8_t *)workspace + p.tail_off) +
+                                          (size_t)b0 * c0->H_q * p.n_tsplit * (4 + c0->d);
     hipError_t e = hipSuccess;
     // timing events: the first split launch's start and the last one's end
     KernelEvents ev;
@@ -439,6 +502,7 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
       ma.H_q = a.H_q;
       ma.Hg = a.Hg;
       ma.n_split = a.n_split;
+      ma.ws_splits = ws_splits;
       ma.split_tokens = a.split_tokens;
       ma.stride = a.stride;
       ma.grid8 = (a.n_split & 7) == 0;
@@ -510,11 +574,77 @@ extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, in
       e = jolt_launch_generic(a, nb, s, ev);
       if (e != hipSuccess) return fail(JOLT_E_HIP, "split kernel launch: %s", hipGetErrorString(e));
     }
+    if (p.n_tsplit > 0) {
+      // the uncompressed tail: flash-decoding splits over its rows, written as
+      // output-space partials [m, l, 0, 0, o/l] into the same merge
+      DenseArgs da;
+      std::memset(&da, 0, sizeof da);
+      da.scale = softmax_scale;
+      da.kv_f32 = tail.dtype == JOLT_F32;
+      da.q_f32 = a.q_f32;
+      da.H = c0->H;
+      da.H_q = c0->H_q;
+      da.Hg = a.Hg;
+      da.d = c0->d;
+      da.T = tail.cap;
+      da.n_split = p.n_tsplit;
+      da.split_tokens = p.tail_split;
+      std::memcpy(da.inv_freq, a.inv_freq, sizeof da.inv_freq);
+      const size_t kvb = (size_t)c0->H * tail.cap * c0->d * (da.kv_f32 ? 4 : 2);
+      da.k = (const uint8_t *)tail.k + b0 * kvb;
+      da.v = (const uint8_t *)tail.v + b0 * kvb;
+      da.q = a.q;
+      da.out = a.out;
+      da.batch = nb;
+      da.seq0 = b0;
+      for (int i = 0; i < nb; ++i) {
+        da.q_pos[i] = q_pos[b0 + i];
+        da.T_seq[i] = tail.len[b0 + i];
+      }
+      if (mfma) {
+        da.ws = a.ws;
+        da.ws_splits = ws_splits;
+        da.split0 = p.n_split;
+      } else {
+        da.ws = (float *)a.tail_ws;
+        da.ws_splits = p.n_tsplit;
+        da.split0 = 0;
+      }
+      e = jolt_launch_dense(da, nb, s);
+      if (e != hipSuccess) return fail(JOLT_E_HIP, "tail kernel launch: %s", hipGetErrorString(e));
+    }
     a.nseq = nb;
-    e = p.kernel == JOLT_KERNEL_MFMA ? jolt_launch_merge_outputs(a, nb, s) : jolt_launch_merge(a, nb, s);
+    e = mfma ? jolt_launch_merge_outputs(a, nb, ws_splits, s) : jolt_launch_merge(a, nb, s);
     if (e != hipSuccess) return fail(JOLT_E_HIP, "merge kernel launch: %s", hipGetErrorString(e));
   }
   return ok();
+}
+
+extern "C" jolt_status jolt_decode_attention(const jolt_cache *const *caches, int32_t batch,
+                                             int32_t layer, const void *q, jolt_dtype q_dtype,
+                                             const int32_t *q_pos, const float *inv_freq,
+                                             float softmax_scale, float *out, void *workspace,
+                                             size_t ws_bytes, const jolt_launch *launch,
+                                             jolt_stream stream) {
+  return decode_impl(caches, batch, layer, q, q_dtype, q_pos, inv_freq, softmax_scale, TailIn{},
+                     out, workspace, ws_bytes, launch, stream);
+}
+
+extern "C" jolt_status jolt_decode_attention_tail(
+    const jolt_cache *const *caches, int32_t batch, int32_t layer, const void *q,
+    jolt_dtype q_dtype, const int32_t *q_pos, const float *inv_freq, float softmax_scale,
+    const void *k_tail, const void *v_tail, jolt_dtype tail_dtype, int32_t tail_cap,
+    const int32_t *tail_len, float *out, void *workspace, size_t ws_bytes,
+    const jolt_launch *launch, jolt_stream stream) {
+  if (tail_cap < 0 || tail_cap > kMaxPos) return fail(JOLT_E_INVALID, "tail_cap=%d", tail_cap);
+  TailIn t;
+  t.k = k_tail;
+  t.v = v_tail;
+  t.dtype = tail_dtype;
+  t.cap = tail_cap;
+  t.len = tail_len;
+  return decode_impl(caches, batch, layer, q, q_dtype, q_pos, inv_freq, softmax_scale, t, out,
+                     workspace, ws_bytes, launch, stream);
 }
 
 // ----------------------------------------------------------------- dense --
@@ -593,7 +723,12 @@ extern "C" jolt_status jolt_dense_attention(const void *k_rope, const void *v, j
     a.ws = (float *)workspace + (size_t)b0 * n_q * n_split * (4 + d);
     a.batch = nb;
     a.seq0 = b0;
-    for (int i = 0; i < nb; ++i) a.q_pos[i] = q_pos[b0 + i];
+    a.ws_splits = n_split;
+    a.split0 = 0;
+    for (int i = 0; i < nb; ++i) {
+      a.q_pos[i] = q_pos[b0 + i];
+      a.T_seq[i] = T;
+    }
     hipError_t e = jolt_launch_dense(a, nb, s);
     if (e != hipSuccess) return fail(JOLT_E_HIP, "dense launch: %s", hipGetErrorString(e));
     e = jolt_launch_dense_merge(a, nb, s);

@@ -18,7 +18,19 @@ constexpr int kMaxHg = 16;      // query heads per KV head
 constexpr int kMaxBatchPerLaunch = 32;
 constexpr int kMaxD = 128;
 constexpr int kMaxSplits = 2048;
+constexpr int kMaxTailSplits = 256;  // splits of an uncompressed tail
 constexpr double kRopeSmall = 128.0;  // radians; see MfmaArgs::rope_small
+
+// Whether a launch with one query per KV head runs the one-query (HG1)
+// variant of its class -- key bits, value bits, key-rank steps of 32 and
+// value-rank blocks of 16 (after padding): the wide-key classes (4 waves)
+// and the value-rank-above-128 classes (8 waves), except 8-bit keys and
+// values with 8 key-rank steps, whose 8-wave variant does not fit its
+// registers and which runs the grouped-query 4-wave class instead.  The
+// launcher and the host's LDS sizing both follow this.
+__host__ __device__ constexpr bool hg1_variant(int bK, int bV, int kt, int nmv) {
+  return kt > 8 || (nmv > 8 && !(bK == 8 && bV == 8 && kt == 8));
+}
 
 struct CellDev {
   // K: A [T_pad][rT_pad] row-major (fp16, scaled, for bf16 caches).
@@ -68,6 +80,10 @@ struct DecodeArgs {
   const void *q;          // [batch][H_q][d]
   float *out;             // [batch][H_q][d]
   float *ws;              // partials [batch][H_q][n_split][stride]
+  // uncompressed-tail partials of the float32 path, [batch][H_q][n_tsplit][4 + d]
+  // (dense layout; n_tsplit = 0: no tail)
+  const float *tail_ws;
+  int32_t n_tsplit;
   float inv_freq[kMaxD / 2];
   float scale;
   int32_t q_f32, f32;     // f32: the caches store float32 factors
@@ -92,11 +108,12 @@ struct SeqMfma {
 // Kernel arguments of one MFMA split-T launch (passed by value).
 struct MfmaArgs {
   const void *q;          // [batch][H_q][d]
-  float *ws;              // partials [batch][H_q][n_split][stride]
+  float *ws;              // partials [batch][H_q][ws_splits][stride] (this launch: the first n_split)
   float inv_freq[kMaxD / 2];
   float scale;
   int32_t q_f32, H, H_q, Hg;
   int32_t n_split, split_tokens, stride, rV_max, nseq;
+  int32_t ws_splits;      // splits per (sequence, query head) row of ws (>= n_split)
   int32_t grid8;          // grid (8 H, n_split / 8, nseq) (n_split % 8 == 0), else (H, n_split, nseq)
   // bit m: every angle t * inv_freq[f] of the launch with 16 m <= f < 16 m + 16
   // is at most kRopeSmall radians (such blocks skip the 2 pi reduction)
@@ -122,13 +139,15 @@ struct DenseArgs {
   const void *v;
   const void *q;
   float *out;
-  float *ws;              // [batch][H_q][n_split][4 + d]
+  float *ws;              // [batch][H_q][ws_splits][4 + d]; this launch's splits start at split0
   float inv_freq[kMaxD / 2];
   float scale;
   int32_t kv_f32, q_f32;
-  int32_t batch, H, H_q, Hg, d, T;
+  int32_t batch, H, H_q, Hg, d, T;  // T: rows per (sequence, head) in k and v
   int32_t n_split, split_tokens;
+  int32_t ws_splits, split0;
   int32_t q_pos[kMaxBatchPerLaunch];
+  int32_t T_seq[kMaxBatchPerLaunch];  // tokens of each sequence (<= T) that are attended to
   int32_t seq0;           // first sequence of this launch
 };
 
@@ -197,7 +216,7 @@ hipError_t jolt_launch_generic(const jolt::DecodeArgs &a, int nseq, hipStream_t 
 hipError_t jolt_launch_mfma(const jolt::MfmaArgs &a, int nseq, int bK, int bV, int nkt,
                             int lds_bytes, hipStream_t s, jolt::KernelEvents ev);
 hipError_t jolt_launch_merge(const jolt::DecodeArgs &a, int nseq, hipStream_t s);
-hipError_t jolt_launch_merge_outputs(const jolt::DecodeArgs &a, int nseq, hipStream_t s);
+hipError_t jolt_launch_merge_outputs(const jolt::DecodeArgs &a, int nseq, int ns, hipStream_t s);
 hipError_t jolt_launch_dense(const jolt::DenseArgs &a, int nseq, hipStream_t s);
 hipError_t jolt_launch_dense_merge(const jolt::DenseArgs &a, int nseq, hipStream_t s);
 hipError_t jolt_launch_unpack(const jolt::LayerDev *layer, int tau, int H, int T, int d,

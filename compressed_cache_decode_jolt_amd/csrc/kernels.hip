@@ -280,12 +280,18 @@ __global__ __launch_bounds__(256) void merge_finalize(DecodeArgs a) {
   const float *pb = a.ws + ((size_t)(b * a.H_q + j) * ns) * a.stride;
   const int st = a.stride;
 
+  // uncompressed-tail partials [m, l, 0, 0, o/l] of this (sequence, query
+  // head), if any: they join the same softmax
+  const int nts = a.n_tsplit, tst = 4 + d;
+  const float *tp = nts > 0 ? a.tail_ws + (size_t)(b * a.H_q + j) * nts * tst : nullptr;
+  __shared__ float wt_s[kMaxTailSplits];
   float mx = -INFINITY;
   for (int s = tid; s < ns; s += 256) {
     float m = pb[(size_t)s * st];
     w_s[s] = m;
     mx = fmaxf(mx, m);
   }
+  for (int s = tid; s < nts; s += 256) mx = fmaxf(mx, tp[(size_t)s * tst]);
   mx = block_reduce(mx, red, true);
   float ls = 0.0f;
   for (int s = tid; s < ns; s += 256) {
@@ -294,7 +300,13 @@ __global__ __launch_bounds__(256) void merge_finalize(DecodeArgs a) {
     w_s[s] = w;
     ls += w * pb[(size_t)s * st + 1];
   }
-  ls = block_reduce(ls, red, false);  // also orders the w_s writes
+  for (int s = tid; s < nts; s += 256) {
+    const float m = tp[(size_t)s * tst];
+    const float w = (m == -INFINITY) ? 0.0f : __expf(m - mx) * tp[(size_t)s * tst + 1];
+    wt_s[s] = w;  // weight of the split's normalised output o/l
+    ls += w;
+  }
+  ls = block_reduce(ls, red, false);  // also orders the w_s / wt_s writes
   const float inv = 1.0f / ls;
 
   split_columns(pb, st, ns, w_s, d, 4 + a.rV_max, inv, cv, tid, 256);
@@ -339,6 +351,10 @@ __global__ __launch_bounds__(256) void merge_finalize(DecodeArgs a) {
     if (f < d)
       for (int i = part; i < d; i += 2) acc += cv[i] * mat[i * d + f];
   }
+  // the tail's share: sum over its splits of w o (o already divided by l)
+  if (f < d)
+    for (int s = part; s < nts; s += 2)
+      if (wt_s[s] > 0.0f) acc += wt_s[s] * inv * tp[(size_t)s * tst + 4 + f];
   if (f < d) ov[part][f] = acc;
   __syncthreads();
   if (tid < d) a.out[((size_t)b * a.H_q + j) * d + tid] = ov[0][tid] + ov[1][tid];
@@ -355,7 +371,7 @@ __global__ __launch_bounds__(256) void dense_split(DenseArgs a) {
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int tg = tid / LPT, li = tid % LPT;
   const int Hg = a.Hg, T = a.T;
-  const int t0 = split * a.split_tokens, t1 = min(T, t0 + a.split_tokens);
+  const int t0 = split * a.split_tokens, t1 = min(a.T_seq[b], t0 + a.split_tokens);
   const int qpos = a.q_pos[b];
   // the workgroup's query heads rotated to q_pos (one pair per thread), scaled
   __shared__ float qs[HG][D];
@@ -490,7 +506,7 @@ __global__ __launch_bounds__(256) void dense_split(DenseArgs a) {
       ls += wt * sl[w][u];
       as += wt * sacc[w][u][f];
     }
-    float *part = a.ws + ((size_t)(b * a.H_q + h * Hg + u) * a.n_split + split) * (4 + D);
+    float *part = a.ws + ((size_t)(b * a.H_q + h * Hg + u) * a.ws_splits + a.split0 + split) * (4 + D);
     if (f == 0) {
       part[0] = mx;
       part[1] = ls;
@@ -517,7 +533,7 @@ __global__ __launch_bounds__(256, 2) void dense_mfma(DenseArgs a) {
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int Hg = a.Hg, T = a.T;
-  const int t0 = split * a.split_tokens, t1 = min(T, t0 + a.split_tokens);
+  const int t0 = split * a.split_tokens, t1 = min(a.T_seq[b], t0 + a.split_tokens);
   __shared__ float qs[16][D];
   __shared__ float Pw[4][16][17];      // per wave: [token][query], padded
   __shared__ float Aw[4][16];          // per wave: rescale factor per query
@@ -662,7 +678,7 @@ __global__ __launch_bounds__(256, 2) void dense_mfma(DenseArgs a) {
       ls += wt * Lw[w][u];
       os += wt * Ow[w][u][f];
     }
-    float *part = a.ws + ((size_t)(b * a.H_q + h * Hg + u) * a.n_split + split) * (4 + D);
+    float *part = a.ws + ((size_t)(b * a.H_q + h * Hg + u) * a.ws_splits + a.split0 + split) * (4 + D);
     if (f == 0) {
       part[0] = mx;
       part[1] = ls;
@@ -821,13 +837,15 @@ hipError_t jolt_launch_dense(const DenseArgs &a, int nseq, hipStream_t s) {
 
 hipError_t jolt_launch_dense_merge(const DenseArgs &a, int nseq, hipStream_t s) {
   hipLaunchKernelGGL(merge_outputs, dim3(a.H_q, nseq), dim3(256), 0, s, (const float *)a.ws, a.out,
-                     a.n_split, a.d, a.H_q);
+                     a.ws_splits, a.d, a.H_q);
   return hipGetLastError();
 }
 
-hipError_t jolt_launch_merge_outputs(const DecodeArgs &a, int nseq, hipStream_t s) {
+// ns: splits per (sequence, query head) row of the workspace (the split
+// kernel's plus any uncompressed-tail splits)
+hipError_t jolt_launch_merge_outputs(const DecodeArgs &a, int nseq, int ns, hipStream_t s) {
   hipLaunchKernelGGL(merge_outputs, dim3(a.H_q, nseq), dim3(256), 0, s, (const float *)a.ws, a.out,
-                     a.n_split, a.d, a.H_q);
+                     ns, a.d, a.H_q);
   return hipGetLastError();
 }
 

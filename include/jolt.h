@@ -161,6 +161,39 @@ jolt_status jolt_decode_attention(const jolt_cache *const *caches, int32_t batch
                                   void *workspace, size_t ws_bytes, const jolt_launch *launch,
                                   jolt_stream stream);
 
+/*
+ * Decode attention over a compressed cache followed by an uncompressed tail
+ * (the tokens generated since the cache was compressed).  The JoLT summary
+ * compresses the prefill cache in one global pass and notes (§5) that this
+ * does not by itself support streaming generation; a decode loop therefore
+ * keeps its newest tokens dense until the next compression.  The query
+ * attends, under one softmax, to the T compressed tokens of its sequence
+ * (keys rotated to positions 0..T-1) and then to the first tail_len[b] rows
+ * of the tail:
+ *   k_tail, v_tail  DEVICE [batch][n_kv_heads][tail_cap][d] in tail_dtype
+ *                   (F32 or BF16); keys already rotated to their own
+ *                   positions (normally T, T+1, ...)
+ *   tail_cap        rows per (sequence, head) of k_tail / v_tail, >= 0
+ *   tail_len        HOST [batch], 0 <= tail_len[b] <= tail_cap
+ * The other arguments are as for jolt_decode_attention; the workspace must
+ * hold jolt_decode_tail_workspace_size bytes for the same tail_cap.  The
+ * tail's partial softmax states join the compressed splits' in the same
+ * merge.  Errors: those of jolt_decode_attention, and JOLT_E_INVALID for a
+ * negative or too large tail_cap, a tail_len outside [0, tail_cap], NULL tail
+ * pointers with tail_cap > 0 or another tail dtype.
+ */
+jolt_status jolt_decode_tail_workspace_size(const jolt_cache *const *caches, int32_t batch,
+                                            int32_t layer, int32_t tail_cap,
+                                            const jolt_launch *launch, size_t *bytes);
+jolt_status jolt_decode_attention_tail(const jolt_cache *const *caches, int32_t batch,
+                                       int32_t layer, const void *q, jolt_dtype q_dtype,
+                                       const int32_t *q_pos, const float *inv_freq,
+                                       float softmax_scale, const void *k_tail,
+                                       const void *v_tail, jolt_dtype tail_dtype,
+                                       int32_t tail_cap, const int32_t *tail_len, float *out,
+                                       void *workspace, size_t ws_bytes,
+                                       const jolt_launch *launch, jolt_stream stream);
+
 /* Workspace bytes jolt_dense_attention needs. */
 jolt_status jolt_dense_workspace_size(int32_t batch, int32_t n_kv, int32_t n_q, int32_t d,
                                       int32_t T, const jolt_launch *launch, size_t *bytes);

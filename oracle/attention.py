@@ -94,6 +94,33 @@ def decode_layer(cache, layer, q, q_pos, inv_freq, scale, Pi=None, heads=None):
     return out
 
 
+def decode_layer_tail(cache, layer, q, q_pos, inv_freq, scale, k_tail, v_tail, Pi=None):
+    """One sequence, one layer, with an uncompressed tail: the query attends
+    to the T compressed tokens (decoded, keys rotated to positions 0..T-1)
+    followed by the tail's n tokens, whose keys k_tail [H, n, d] are given
+    already rotated to their positions, and values v_tail [H, n, d].  One
+    softmax over all T + n tokens.  (A decode loop appends each generated
+    token's key and value to such a tail until the next compression; the
+    JoLT summary's §5 notes that its prefill compressor alone does not
+    cover streaming generation.)"""
+    d, H, H_q, T = cache["d"], cache["H"], cache["H_q"], cache["T"]
+    if Pi is None:
+        Pi = rotation(cache["rotation_seed"], d)
+    g, lp = group_of(cache, layer)
+    cK, cV = cache["cells"][g]
+    Hg = H_q // H
+    qr = rope(np.asarray(q, dtype=np.float64), q_pos, inv_freq)
+    Khat = decode_cell(cK, lp, d, Pi)
+    Vhat = decode_cell(cV, lp, d, Pi)
+    out = np.empty((H_q, d))
+    for h in range(H):
+        Kr = np.concatenate([rope(Khat[h], np.arange(T), inv_freq),
+                             np.asarray(k_tail[h], dtype=np.float64)])
+        V = np.concatenate([Vhat[h], np.asarray(v_tail[h], dtype=np.float64)])
+        out[h * Hg:(h + 1) * Hg] = softmax_attention(qr[h * Hg:(h + 1) * Hg], Kr, V, scale)
+    return out
+
+
 def decode_attention(caches, layer, q, q_pos, inv_freq, scale):
     """Batch of sequences: q [B, H_q, d], q_pos [B] -> [B, H_q, d]."""
     Pi_cache = {}

@@ -190,3 +190,61 @@ def test_residual_improves_attention():
         cache = compress(groups, [((8, 8, b), (8, 8, b))], "f32", 1, H_q, [0, 1])
         errs.append(np.linalg.norm(att.decode_layer(cache, 0, q, T, inv, 0.2) - raw))
     assert errs[0] > errs[1] > errs[2]
+
+
+# ------------------------------------------------------------ dense tail --
+def _tail_case(seed, n):
+    from oracle.compress import compress
+    g = np.random.default_rng(seed)
+    T, d, H, H_q = 40, 16, 2, 4
+    X = [gen.kv_tensor((94, seed, 0, tau), 1, H, T, d, 1.0 - 0.7 * tau, tau == 0, 1, rank=8)
+         for tau in (0, 1)]
+    c = compress([tuple(X)], [((16, 8, 4), (16, 8, 2))], "f32", 5, H_q, [0, 1])
+    inv = gen.rope_inv_freq_input(1e4, d)
+    q = g.standard_normal((H_q, d))
+    kt = g.standard_normal((H, n, d))
+    vt = g.standard_normal((H, n, d)) * 2
+    return c, inv, q, kt, vt
+
+
+def test_tail_of_length_zero_is_the_compressed_decode():
+    c, inv, q, kt, vt = _tail_case(0, 0)
+    a = att.decode_layer_tail(c, 0, q, 40, inv, 0.3, kt, vt)
+    b = att.decode_layer(c, 0, q, 40, inv, 0.3)
+    assert np.allclose(a, b, rtol=0, atol=1e-13)
+
+
+def test_tail_duplicating_the_prefix_changes_nothing():
+    """Attending to every token twice (the tail repeats the decoded, rotated
+    prefix) gives the same softmax average."""
+    c, inv, q, _, _ = _tail_case(1, 0)
+    Pi = rotation(5, 16)
+    K = att.decode_cell(c["cells"][0][0], 0, 16, Pi)
+    V = att.decode_cell(c["cells"][0][1], 0, 16, Pi)
+    kt = np.stack([rope(K[h], np.arange(40), inv) for h in range(2)])
+    a = att.decode_layer_tail(c, 0, q, 40, inv, 0.3, kt, V)
+    b = att.decode_layer(c, 0, q, 40, inv, 0.3)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+def test_tail_equals_merge_of_two_softmax_partials():
+    """The (max, sum) merge of a partial over the prefix and one over the
+    tail is the softmax over both: brute force on the pieces."""
+    c, inv, q, kt, vt = _tail_case(2, 7)
+    Pi = rotation(5, 16)
+    K = att.decode_cell(c["cells"][0][0], 0, 16, Pi)
+    V = att.decode_cell(c["cells"][0][1], 0, 16, Pi)
+    qr = rope(q, 40, inv)
+    want = att.decode_layer_tail(c, 0, q, 40, inv, 0.3, kt, vt)
+    for j in range(4):
+        h = j // 2
+        parts = []
+        for Kx, Vx in ((rope(K[h], np.arange(40), inv), V[h]), (kt[h], vt[h])):
+            s = 0.3 * Kx @ qr[j]
+            m = s.max()
+            p = np.exp(s - m)
+            parts.append((m, p.sum(), p @ Vx))
+        M = max(m for m, _, _ in parts)
+        num = sum(np.exp(m - M) * o for m, _, o in parts)
+        den = sum(np.exp(m - M) * l for m, l, _ in parts)
+        assert np.allclose(num / den, want[j], rtol=1e-12, atol=1e-12)
