@@ -37,20 +37,37 @@ def splitmix64(seed, n):
     return out
 
 
+def splitmix64_array(seed, n):
+    """The same n outputs as splitmix64, computed as an array: output i is the
+    mixing function of the state seed + (i + 1) * 0x9E3779B97F4A7C15
+    (mod 2^64), uint64 arithmetic wrapping as the generator's does."""
+    with np.errstate(over="ignore"):
+        st = np.uint64(seed & _M64) + (np.arange(1, n + 1, dtype=np.uint64) *
+                                        np.uint64(0x9E3779B97F4A7C15))
+        z = (st ^ (st >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+        return z ^ (z >> np.uint64(31))
+
+
 def uniforms(seed, n):
-    xs = np.array(splitmix64(seed, n), dtype=np.uint64)
+    xs = splitmix64_array(seed, n)
     return ((xs >> np.uint64(11)).astype(np.float64) + 0.5) * (2.0 ** -53)
 
 
-def gaussian_matrix(seed, d):
-    n = d * d
+def gaussians(seed, n):
+    """First n standard normals of the seeded stream: consecutive uniform
+    pairs (u1, u2) -> sqrt(-2 ln u1) (cos 2 pi u2, sin 2 pi u2)."""
     u = uniforms(seed, n + (n & 1))
     u1, u2 = u[0::2], u[1::2]
     rad = np.sqrt(-2.0 * np.log(u1))
     z = np.empty(u.shape[0])
     z[0::2] = rad * np.cos(2.0 * np.pi * u2)
     z[1::2] = rad * np.sin(2.0 * np.pi * u2)
-    return z[:n].reshape(d, d)
+    return z[:n]
+
+
+def gaussian_matrix(seed, d):
+    return gaussians(seed, d * d).reshape(d, d)
 
 
 def rotation(seed, d):

@@ -58,3 +58,16 @@ def test_seed_determinism():
     a = rotation.rotation(5, 64)
     assert np.array_equal(a, rotation.rotation(5, 64))
     assert np.max(np.abs(a - rotation.rotation(6, 64))) > 0.1
+
+
+def test_array_form_of_the_generator_equals_the_sequential_one():
+    from oracle.rotation import splitmix64, splitmix64_array
+    for seed in (0, 1, 0x4A4F4C54, (1 << 64) - 1):
+        assert splitmix64_array(seed, 257).tolist() == splitmix64(seed, 257)
+
+
+def test_gaussian_stream_prefix_and_moments():
+    from oracle.rotation import gaussian_matrix, gaussians
+    z = gaussians(9, 200001)
+    assert np.array_equal(gaussian_matrix(9, 16).ravel(), z[:256])
+    assert abs(z.mean()) < 5 / np.sqrt(len(z)) and abs(z.var() - 1) < 0.02
