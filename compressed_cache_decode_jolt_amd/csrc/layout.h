@@ -140,5 +140,6 @@ struct Staged {
 void stage_cache(const jolt_cache_desc *desc, Staged *out, int threads = 0);
 
 void make_rotation(uint64_t seed, int d, double *out);
+void gaussian_fill(uint64_t seed, size_t n, double *out);
 
 }  // namespace jolt

@@ -17,7 +17,10 @@
 
 namespace jolt {
 
-void make_rotation(uint64_t seed, int d, double *out) {
+// The first n normals of the stream seeded with `seed`: SplitMix64 outputs
+// -> uniforms ((x >> 11) + 0.5) 2^-53 -> Box-Muller on consecutive pairs
+// (u1, u2): sqrt(-2 ln u1) cos(2 pi u2), then sin(2 pi u2).
+void gaussian_fill(uint64_t seed, size_t n, double *out) {
   uint64_t state = seed;
   auto next = [&state]() {
     state += 0x9E3779B97F4A7C15ULL;
@@ -26,22 +29,23 @@ void make_rotation(uint64_t seed, int d, double *out) {
     z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
     return z ^ (z >> 31);
   };
-  const int n = d * d;
   const double two_pi = 2.0 * M_PI;
-  // column-major working copy: R[c * d + r]
-  std::vector<double> R(n);
-  for (int k = 0; k < n; k += 2) {
+  for (size_t k = 0; k < n; k += 2) {
     double u1 = ((double)(next() >> 11) + 0.5) * 0x1p-53;
     double u2 = ((double)(next() >> 11) + 0.5) * 0x1p-53;
     double rad = std::sqrt(-2.0 * std::log(u1));
-    double z0 = rad * std::cos(two_pi * u2), z1 = rad * std::sin(two_pi * u2);
-    int r0 = k / d, c0 = k % d;
-    R[(size_t)c0 * d + r0] = z0;
-    if (k + 1 < n) {
-      int r1 = (k + 1) / d, c1 = (k + 1) % d;
-      R[(size_t)c1 * d + r1] = z1;
-    }
+    out[k] = rad * std::cos(two_pi * u2);
+    if (k + 1 < n) out[k + 1] = rad * std::sin(two_pi * u2);
   }
+}
+
+void make_rotation(uint64_t seed, int d, double *out) {
+  const int n = d * d;
+  // the Gaussian matrix row by row, then a column-major working copy R[c * d + r]
+  std::vector<double> Z(n), R(n);
+  gaussian_fill(seed, (size_t)n, Z.data());
+  for (int r = 0; r < d; ++r)
+    for (int c = 0; c < d; ++c) R[(size_t)c * d + r] = Z[(size_t)r * d + c];
   // Householder: for column k, v = x - alpha e_k with alpha = -sign(x_k)|x|.
   std::vector<double> V((size_t)d * d, 0.0), vn2(d, 0.0), diag(d, 0.0);
   for (int k = 0; k < d; ++k) {

@@ -206,7 +206,7 @@ def test_mixed_bits_batch_on_mfma(split):
         assert np.max(np.abs(got[b] - want[b])) <= 2e-2
 
 
-WIDE_KEYS = [((320, 64, 0), (64, 32, 2)), ((384, 32, 2), (192, 48, 8)),
+WIDE_KEYS = [((320, 64, 0), (64, 32, 2)), ((384, 32, 2), (128, 48, 8)),
              ((448, 64, 4), (128, 64, 0)), ((512, 96, 8), (64, 32, 4))]
 
 
@@ -223,6 +223,23 @@ def test_wide_key_ranks_on_mfma(aK, aV, split):
     want = oracle_decode([c], 0, q, [T], inv, 0.088)
     r, mx = rel_l2(got, want), float(np.max(np.abs(got - want)))
     assert r <= 5e-3 and mx <= 2e-2, (r, mx)
+
+
+def test_grouped_wide_keys_with_wide_values_take_the_float32_kernel():
+    """Grouped queries with key ranks above 256 and value ranks above 128 are
+    not an MFMA class (it would not fit a SIMD's registers): forcing the MFMA
+    kernel is refused, the automatic choice runs the float32 kernel and
+    matches the oracle at its tolerance."""
+    d, H, H_q, T = 128, 4, 16, 700
+    c = gen.small_cache(97, T, H, H_q, d, [((384, 32, 2), (192, 48, 8))], [1])
+    inv = gen.rope_inv_freq_input(5e5, d)
+    q = gen.queries(91, 2, 8, H_q, d, "bf16")[None]
+    h = J.jolt_load_cache(c)
+    with pytest.raises(J.JoltError):
+        J.jolt_decode_workspace_size([h], 0, kernel=J.KERNEL_MFMA)
+    got = run_decode([c], 0, q, [T], inv, 0.088, handles=[h])
+    want = oracle_decode([c], 0, q, [T], inv, 0.088)
+    assert rel_l2(got, want) <= 1e-5
 
 
 ONE_QUERY = [((64, 64, 0), (320, 64, 4)), ((192, 48, 8), (512, 96, 2)),
