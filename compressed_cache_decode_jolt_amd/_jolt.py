@@ -37,6 +37,11 @@ class jolt_cache_desc(C.Structure):
                 ("rotation_seed", C.c_uint64), ("cells", C.POINTER(jolt_cell))]
 
 
+class jolt_flash_params(C.Structure):
+    _fields_ = [("q_cap", C.c_int32), ("oversample", C.c_int32), ("power_iters", C.c_int32),
+                ("sketch_seed", C.c_uint64)]
+
+
 class jolt_launch(C.Structure):
     _fields_ = [("kernel", C.c_int32), ("split_tokens", C.c_int32),
                 ("ev_begin", C.c_void_p), ("ev_end", C.c_void_p),
@@ -70,6 +75,16 @@ EXPORTS = {
                              [C.c_void_p, C.c_int, C.POINTER(C.c_int32), C.POINTER(C.c_float),
                               C.c_float, C.c_void_p, C.c_void_p, C.c_size_t,
                               C.POINTER(jolt_launch), C.c_void_p]),
+    "jolt_flash_spectra": (C.c_int, [C.c_void_p, C.c_int, C.c_int32, C.c_int32, C.c_int32,
+                                     C.c_int32, C.POINTER(jolt_flash_params), C.c_void_p,
+                                     C.c_void_p, C.c_void_p, C.c_void_p]),
+    "jolt_flash_compress_cell": (C.c_int, [C.c_void_p, C.c_int, C.c_int32, C.c_int32, C.c_int32,
+                                           C.c_int32, C.POINTER(jolt_flash_params), C.c_int32,
+                                           C.c_int32, C.c_int32, C.c_uint64, C.c_int, C.c_void_p,
+                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                           C.c_void_p]),
+    "jolt_quantize_rows": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_void_p,
+                                     C.c_void_p, C.c_void_p]),
     "jolt_last_error": (C.c_char_p, []),
     "jolt_make_rotation": (C.c_int, [C.c_uint64, C.c_int32, C.POINTER(C.c_double)]),
     "jolt_debug_unpack": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
@@ -369,3 +384,75 @@ def jolt_debug_sincos(angles, variant=0):
     _check(lib().jolt_debug_sincos(x.ctypes.data, x.size, sn.ctypes.data, cs.ctypes.data,
                                    int(variant)))
     return sn, cs
+
+
+# ------------------------------------------------------------- compressor --
+def _flash_params(q_cap, oversample, power_iters, sketch_seed):
+    return jolt_flash_params(int(q_cap), int(oversample), int(power_iters), int(sketch_seed))
+
+
+def _cell_tensor(X):
+    import torch
+    if not isinstance(X, torch.Tensor) or X.dim() != 4 or not X.is_cuda or not X.is_contiguous():
+        raise ValueError("X must be a contiguous GPU tensor [group_size, H, T, d]")
+    if X.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(X.dtype)
+    return X
+
+
+def jolt_flash_spectra(X, q_cap, oversample=16, power_iters=2, sketch_seed=0, stream=None):
+    """FlashJoLT allocator inputs of one cell X (device [group_size, H, T, d]):
+    (sT2 [q_cap + 1] with the synthetic tail entry last, sF2 [d], norm2)."""
+    X = _cell_tensor(X)
+    gs, H, T, d = X.shape
+    sT2 = np.empty(q_cap + 1, dtype=np.float64)
+    sF2 = np.empty(d, dtype=np.float64)
+    n2 = C.c_double()
+    P = _flash_params(q_cap, oversample, power_iters, sketch_seed)
+    _check(lib().jolt_flash_spectra(_ptr(X), _dtype_code(X), gs, H, T, d, C.byref(P),
+                                    sT2.ctypes.data, sF2.ctypes.data, C.addressof(n2),
+                                    _stream(stream)))
+    return sT2, sF2, n2.value
+
+
+def jolt_flash_compress_cell(X, r_T, r_F, bits, q_cap, rotation_seed, factor_dtype="bf16",
+                             oversample=16, power_iters=2, sketch_seed=0, stream=None):
+    """Compress one cell X (device [group_size, H, T, d]) on the GPU.  Returns a
+    cell dict as jolt_load_cache takes it: r_T, r_F, bits, A, B, G (float32
+    arrays holding the stored factor values), codes (uint8) and scales."""
+    X = _cell_tensor(X)
+    gs, H, T, d = X.shape
+    fdt = JOLT_F32 if factor_dtype == "f32" else JOLT_BF16
+    sto = np.float32 if factor_dtype == "f32" else np.uint16
+    A = np.zeros((T, r_T), dtype=sto)
+    B = np.zeros((d, r_F), dtype=sto)
+    G = np.zeros((gs, H, r_T, r_F), dtype=sto)
+    codes = np.zeros((gs, H, T, d * bits // 8), dtype=np.uint8) if bits else None
+    scales = np.zeros((gs, H, T), dtype=np.float32) if bits else None
+    P = _flash_params(q_cap, oversample, power_iters, sketch_seed)
+    _check(lib().jolt_flash_compress_cell(
+        _ptr(X), _dtype_code(X), gs, H, T, d, C.byref(P), int(r_T), int(r_F), int(bits),
+        C.c_uint64(int(rotation_seed)), fdt, A.ctypes.data, B.ctypes.data, G.ctypes.data,
+        codes.ctypes.data if bits else None, scales.ctypes.data if bits else None,
+        _stream(stream)))
+
+    def vals(a):
+        if factor_dtype == "f32":
+            return a
+        return (a.astype(np.uint32) << 16).view(np.float32)
+    return {"r_T": int(r_T), "r_F": int(r_F), "bits": int(bits), "A": vals(A), "B": vals(B),
+            "G": vals(G), "codes": codes, "scales": scales}
+
+
+def jolt_quantize_rows(rows, bits, stream=None):
+    """rows: device float64 [n, d] (rotated residual rows) -> (codes uint8
+    [n, d*bits/8], scales float32 [n]) device tensors."""
+    import torch
+    if rows.dtype != torch.float64 or not rows.is_cuda or not rows.is_contiguous() or rows.dim() != 2:
+        raise ValueError("rows must be a contiguous float64 GPU tensor [n, d]")
+    n, d = rows.shape
+    codes = torch.empty((n, d * bits // 8), dtype=torch.uint8, device=rows.device)
+    scales = torch.empty((n,), dtype=torch.float32, device=rows.device)
+    _check(lib().jolt_quantize_rows(_ptr(rows), n, d, int(bits), _ptr(codes), _ptr(scales),
+                                    _stream(stream)))
+    return codes, scales

@@ -46,6 +46,20 @@ static jolt_status ok() {
   g_err.clear();
   return JOLT_OK;
 }
+// The same for the other translation units of the library (JOLT_OK clears
+// the message).
+namespace jolt {
+jolt_status set_error(jolt_status st, const char *fmt, ...) {
+  if (st == JOLT_OK) return ok();
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+}  // namespace jolt
 
 #define HIP_TRY(expr)                                                               \
   do {                                                                              \

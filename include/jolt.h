@@ -214,6 +214,58 @@ jolt_status jolt_dense_attention(const void *k_rope, const void *v, jolt_dtype k
                                  void *workspace, size_t ws_bytes, const jolt_launch *launch,
                                  jolt_stream stream);
 
+/*
+ * GPU compressor (FlashJoLT).  "A JoLT for the KV cache" (arXiv 2607.12550v4
+ * summary), §3 and §3.1 "Fast variant: FlashJoLT": ST-HOSVD of one cell whose
+ * token-mode SVD is a randomized SVD of the leading q_cap directions
+ * (randomized subspace iteration with a seeded Gaussian test matrix of
+ * q_cap + oversample columns and power_iters iterations), exact feature-mode
+ * SVD, residual against the stored factors rotated by the seeded Pi and
+ * quantised to b bits.  X is one cell's grouped cache, DEVICE
+ * [group_size][n_kv_heads][T][head_dim] in x_dtype (F32 or BF16); all
+ * arithmetic is float64.  Synchronous on `stream`; allocates its own device
+ * scratch (a prefill-time operation, not for capture).
+ */
+typedef struct {
+  int32_t q_cap;        /* token-mode directions computed; also the largest r_T  */
+  int32_t oversample;   /* extra sketch columns (>= 0)                          */
+  int32_t power_iters;  /* subspace iterations (0..16)                          */
+  uint64_t sketch_seed; /* seed of the Gaussian test matrix (SplitMix64 stream, */
+                        /* Box-Muller, row by row as for the rotation)          */
+} jolt_flash_params;
+
+/* Allocator inputs of one cell: HOST sT2[q_cap + 1] (the q_cap leading squared
+ * token-mode singular values, descending, then the synthetic tail entry
+ * max(||X||^2 - their sum, 0)), HOST sF2[head_dim] (squared feature-mode
+ * singular values of the unprojected tensor, descending), HOST *norm2.
+ * Errors: JOLT_E_INVALID (shape, params, NULL), JOLT_E_HIP. */
+jolt_status jolt_flash_spectra(const void *X, jolt_dtype x_dtype, int32_t group_size,
+                               int32_t n_kv_heads, int32_t T, int32_t head_dim,
+                               const jolt_flash_params *params, double *sT2, double *sF2,
+                               double *norm2, jolt_stream stream);
+
+/* Compress one cell at (r_T <= q_cap, r_F, bits) into HOST buffers in the
+ * layout of jolt_cell: A [T][r_T], B [head_dim][r_F], G [group_size][H][r_T][r_F]
+ * in factor_dtype (F32, or BF16 as its 16-bit patterns), codes
+ * [group_size][H][T][head_dim*bits/8] packed least significant bits first
+ * and scales [group_size][H][T] (unused when bits == 0; A, B, G unused when
+ * r_T == 0).  Errors: JOLT_E_INVALID (ranks, bits, dtype, NULL), JOLT_E_HIP. */
+jolt_status jolt_flash_compress_cell(const void *X, jolt_dtype x_dtype, int32_t group_size,
+                                     int32_t n_kv_heads, int32_t T, int32_t head_dim,
+                                     const jolt_flash_params *params, int32_t r_T, int32_t r_F,
+                                     int32_t bits, uint64_t rotation_seed,
+                                     jolt_dtype factor_dtype, void *A, void *B, void *G,
+                                     uint8_t *codes, float *scales, jolt_stream stream);
+
+/* The quantiser and packer alone, on rotated residual rows: DEVICE rows
+ * [n_rows][d] float64 -> DEVICE codes [n_rows][d*bits/8] and scales [n_rows]:
+ * delta = fl32(2 max|r| / (2^b - 1)), c = clip(rint(r / delta + (2^b - 1)/2))
+ * with ties to even (delta = 0: c = floor((2^b - 1)/2)), packed least
+ * significant bits first.  Asynchronous on `stream`.  Errors: JOLT_E_INVALID
+ * (d not in 2..128, bits not 2/4/8, NULL), JOLT_E_HIP. */
+jolt_status jolt_quantize_rows(const double *rows, int64_t n_rows, int32_t d, int32_t bits,
+                               uint8_t *codes, float *scales, jolt_stream stream);
+
 /* Thread-local description of the last error of this thread ("" if none). */
 const char *jolt_last_error(void);
 

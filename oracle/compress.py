@@ -31,6 +31,12 @@ from .tucker import reconstruct, spectra, st_hosvd
 
 def compress_cell(X, r_T, r_F, bits, factor_dtype, Pi):
     A, B, G = st_hosvd(X, r_T, r_F)
+    return residual_cell(X, A, B, G, r_T, r_F, bits, factor_dtype, Pi)
+
+
+def residual_cell(X, A, B, G, r_T, r_F, bits, factor_dtype, Pi):
+    """Stored cell from exact factors: rounded to the storage dtype, then the
+    residual against that stored reconstruction rotated, quantised, packed."""
     A, B, G = round_to(A, factor_dtype), round_to(B, factor_dtype), round_to(G, factor_dtype)
     keep = np.float64 if factor_dtype == "f64" else np.float32
     cell = {"r_T": int(r_T), "r_F": int(r_F), "bits": int(bits),

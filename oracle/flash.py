@@ -90,3 +90,12 @@ def flash_st_hosvd(X, r_T, r_F, q_cap, oversample=16, power_iters=2, sketch_seed
     B = V[:, np.argsort(w)[::-1][:r_F]]
     G = Y @ B
     return A, B, G
+
+
+def flash_compress_cell(X, r_T, r_F, bits, factor_dtype, Pi, q_cap, oversample=16, power_iters=2,
+                        sketch_seed=0):
+    """One stored cell as oracle.compress.compress_cell builds it, with the
+    FlashJoLT token basis in place of the exact one."""
+    from .compress import residual_cell
+    A, B, G = flash_st_hosvd(X, r_T, r_F, q_cap, oversample, power_iters, sketch_seed)
+    return residual_cell(X, A, B, G, r_T, r_F, bits, factor_dtype, Pi)
