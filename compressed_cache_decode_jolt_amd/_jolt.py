@@ -85,6 +85,11 @@ EXPORTS = {
                                            C.c_void_p]),
     "jolt_quantize_rows": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_void_p,
                                      C.c_void_p, C.c_void_p]),
+    "jolt_noalloc_scratch_bytes": (C.c_size_t, []),
+    "jolt_decode_attention_noalloc": (C.c_int, [C.POINTER(C.c_void_p), C.c_int32, C.c_int32,
+                                                C.c_void_p, C.c_int, C.POINTER(C.c_int32),
+                                                C.POINTER(C.c_float), C.c_float, C.c_void_p,
+                                                C.POINTER(jolt_launch), C.c_void_p]),
     "jolt_last_error": (C.c_char_p, []),
     "jolt_make_rotation": (C.c_int, [C.c_uint64, C.c_int32, C.POINTER(C.c_double)]),
     "jolt_debug_unpack": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
@@ -294,6 +299,34 @@ def jolt_decode_attention(caches, layer, q, q_pos, inv_freq, softmax_scale, out,
         inv.ctypes.data_as(C.POINTER(C.c_float)), C.c_float(softmax_scale), _ptr(out),
         _ptr(_workspace(workspace)), _nbytes(workspace), C.byref(L) if L else None,
         _stream(stream)))
+
+
+def jolt_noalloc_scratch_bytes():
+    return int(lib().jolt_noalloc_scratch_bytes())
+
+
+def jolt_decode_attention_noalloc(caches, layer, q, q_pos, inv_freq, softmax_scale, out,
+                                  kernel=None, split_tokens=0, stream=None, deterministic=False):
+    """jolt_decode_attention with the split partials in the library's own
+    static device buffer (no workspace argument, no allocation)."""
+    import torch
+    B = len(caches)
+    if B:
+        m = caches[0].meta
+        shape = (B, m["H_q"], m["d"])
+        _check_tensor("q", q, (torch.float32, torch.bfloat16), shape)
+        _check_tensor("out", out, (torch.float32,), shape)
+        if len(q_pos) != B:
+            raise ValueError(f"q_pos has {len(q_pos)} entries for {B} sequences")
+        inv = _inv_freq(inv_freq, m["d"])
+    else:
+        inv = np.zeros(1, dtype=np.float32)
+    qp = (C.c_int32 * max(1, B))(*[int(x) for x in q_pos])
+    L = _launch(kernel, split_tokens, None, deterministic)
+    _check(lib().jolt_decode_attention_noalloc(
+        _handles(caches), B, layer, _ptr(q), _dtype_code(q), qp,
+        inv.ctypes.data_as(C.POINTER(C.c_float)), C.c_float(softmax_scale), _ptr(out),
+        C.byref(L) if L else None, _stream(stream)))
 
 
 def jolt_decode_tail_workspace_size(caches, layer, tail_cap, kernel=None, split_tokens=0):

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -659,6 +660,57 @@ extern "C" jolt_status jolt_decode_attention_tail(
   t.len = tail_len;
   return decode_impl(caches, batch, layer, q, q_dtype, q_pos, inv_freq, softmax_scale, t, out,
                      workspace, ws_bytes, launch, stream);
+}
+
+// ------------------------------------------------- allocation-free decode --
+// The split partials of jolt_decode_attention_noalloc live in this file-scope
+// device array.  Every GPU the library runs on holds its own copy (until the
+// process ends); host code never passes the array's name to a kernel -- its
+// per-device address comes from hipGetSymbolAddress, taken once per device
+// with that device current.
+static constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+static jolt_status scratch_address(void **out) {
+  static std::mutex mu;
+  static void *addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(JOLT_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(JOLT_E_UNSUPPORTED, "device index %d >= 64", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(JOLT_E_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return JOLT_OK;
+}
+
+extern "C" size_t jolt_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" jolt_status jolt_decode_attention_noalloc(const jolt_cache *const *caches, int32_t batch,
+                                                     int32_t layer, const void *q, jolt_dtype q_dtype,
+                                                     const int32_t *q_pos, const float *inv_freq,
+                                                     float softmax_scale, float *out,
+                                                     const jolt_launch *launch, jolt_stream stream) {
+  Plan p;
+  jolt_status st = plan_decode(caches, batch, layer, launch, 0, &p);
+  if (st != JOLT_OK) return st;
+  if (p.ws_bytes > kScratchBytes)
+    return fail(JOLT_E_WORKSPACE,
+                "this call needs %zu bytes of split partials; the allocation-free entry point "
+                "holds at most %zu (use jolt_decode_attention with a workspace)",
+                p.ws_bytes, kScratchBytes);
+  if (batch == 0) return ok();
+  void *ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != JOLT_OK) return st;
+  return decode_impl(caches, batch, layer, q, q_dtype, q_pos, inv_freq, softmax_scale, TailIn{},
+                     out, ws, kScratchBytes, launch, stream);
 }
 
 // ----------------------------------------------------------------- dense --

@@ -194,6 +194,27 @@ jolt_status jolt_decode_attention_tail(const jolt_cache *const *caches, int32_t 
                                        void *workspace, size_t ws_bytes,
                                        const jolt_launch *launch, jolt_stream stream);
 
+/*
+ * jolt_decode_attention without a workspace argument, for callers that cannot
+ * allocate device memory: code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid allocation.  The split partials go to
+ * a device array inside the library of jolt_noalloc_scratch_bytes() bytes
+ * (16 MiB), one per GPU, held until the process ends; the call makes no
+ * allocation of any kind.  Every call on a GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (different streams, or a graph
+ * replayed while another call runs) race and may return wrong results --
+ * order them on one stream.  The array needs no clearing between calls.
+ * Errors: those of jolt_decode_attention, and JOLT_E_WORKSPACE when the call
+ * would need more partials than the array holds (fewer splits, a smaller
+ * batch or the workspace entry point then).
+ */
+size_t jolt_noalloc_scratch_bytes(void);
+jolt_status jolt_decode_attention_noalloc(const jolt_cache *const *caches, int32_t batch,
+                                          int32_t layer, const void *q, jolt_dtype q_dtype,
+                                          const int32_t *q_pos, const float *inv_freq,
+                                          float softmax_scale, float *out,
+                                          const jolt_launch *launch, jolt_stream stream);
+
 /* Workspace bytes jolt_dense_attention needs. */
 jolt_status jolt_dense_workspace_size(int32_t batch, int32_t n_kv, int32_t n_q, int32_t d,
                                       int32_t T, const jolt_launch *launch, size_t *bytes);
