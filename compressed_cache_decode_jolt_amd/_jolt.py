@@ -42,6 +42,14 @@ class jolt_flash_params(C.Structure):
                 ("sketch_seed", C.c_uint64)]
 
 
+class jolt_alloc_cell(C.Structure):
+    _fields_ = [("T", C.c_int32), ("d", C.c_int32), ("group_size", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("factor_bytes", C.c_int32),
+                ("n_sT2", C.c_int32), ("sT2", C.POINTER(C.c_double)),
+                ("n_sF2", C.c_int32), ("sF2", C.POINTER(C.c_double)),
+                ("norm2", C.c_double), ("cap", C.c_int32)]
+
+
 class jolt_launch(C.Structure):
     _fields_ = [("kernel", C.c_int32), ("split_tokens", C.c_int32),
                 ("ev_begin", C.c_void_p), ("ev_end", C.c_void_p),
@@ -90,6 +98,8 @@ EXPORTS = {
                                                 C.c_void_p, C.c_int, C.POINTER(C.c_int32),
                                                 C.POINTER(C.c_float), C.c_float, C.c_void_p,
                                                 C.POINTER(jolt_launch), C.c_void_p]),
+    "jolt_allocate": (C.c_int, [C.POINTER(jolt_alloc_cell), C.c_int32, C.c_double,
+                                C.POINTER(C.c_int32), C.POINTER(C.c_double)]),
     "jolt_last_error": (C.c_char_p, []),
     "jolt_make_rotation": (C.c_int, [C.c_uint64, C.c_int32, C.POINTER(C.c_double)]),
     "jolt_debug_unpack": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
@@ -489,3 +499,24 @@ def jolt_quantize_rows(rows, bits, stream=None):
     _check(lib().jolt_quantize_rows(_ptr(rows), n, d, int(bits), _ptr(codes), _ptr(scales),
                                     _stream(stream)))
     return codes, scales
+
+
+def jolt_allocate(cells, budget):
+    """cells: list of dicts with T, d, group_size, H, factor_bytes, sT2, sF2,
+    norm2 and optional cap.  Returns ([(r_T, r_F, bits)], lambda)."""
+    n = len(cells)
+    arr = (jolt_alloc_cell * max(1, n))()
+    keep = []
+    for i, c in enumerate(cells):
+        sT2 = np.ascontiguousarray(c["sT2"], dtype=np.float64)
+        sF2 = np.ascontiguousarray(c["sF2"], dtype=np.float64)
+        keep += [sT2, sF2]
+        arr[i] = jolt_alloc_cell(int(c["T"]), int(c["d"]), int(c["group_size"]), int(c["H"]),
+                                 int(c["factor_bytes"]), sT2.size,
+                                 sT2.ctypes.data_as(C.POINTER(C.c_double)), sF2.size,
+                                 sF2.ctypes.data_as(C.POINTER(C.c_double)), float(c["norm2"]),
+                                 int(c.get("cap") or 0))
+    out = (C.c_int32 * max(1, 3 * n))()
+    lam = C.c_double()
+    _check(lib().jolt_allocate(arr, n, C.c_double(float(budget)), out, C.byref(lam)))
+    return [tuple(out[3 * i:3 * i + 3]) for i in range(n)], lam.value

@@ -287,6 +287,32 @@ jolt_status jolt_flash_compress_cell(const void *X, jolt_dtype x_dtype, int32_t 
 jolt_status jolt_quantize_rows(const double *rows, int64_t n_rows, int32_t d, int32_t bits,
                                uint8_t *codes, float *scales, jolt_stream stream);
 
+/*
+ * Rank/bit allocation (host only, no GPU): "A JoLT for the KV cache" §3 --
+ * one Lagrange multiplier prices bytes for all cells; each cell takes the
+ * (r_T, r_F, bits) minimising estimated error + lambda * bytes, and lambda
+ * is bisected (in log space) to the smallest value whose total bytes fit the
+ * budget.  A cell's error estimate is min(||X||^2, tail_T(r_T) + tail_F(r_F))
+ * times phi(bits) = 1 (b = 0) or m2(d) / (3 (2^b - 1)^2), m2(d) = E[max_i
+ * z_i^2] for z ~ N(0, I_d); ranks on a grid of 16 (r_T = 0 iff r_F = 0),
+ * r_T up to min(T, group_size H d, cap); bits in {0, 2, 4, 8}.  Cells take
+ * their spectra from jolt_flash_spectra (cap = q_cap) or an exact SVD.
+ * HOST cells[n_cells]; HOST choice[n_cells][3] receives (r_T, r_F, bits);
+ * *lambda (may be NULL) the multiplier.  Errors: JOLT_E_INVALID (bad cell,
+ * budget below what rank 0 and no residual would need).
+ */
+typedef struct {
+  int32_t T, d, group_size, n_kv_heads, factor_bytes; /* factor bytes: 2 or 4 */
+  int32_t n_sT2;
+  const double *sT2; /* squared token-mode singular values, descending        */
+  int32_t n_sF2;
+  const double *sF2; /* squared feature-mode singular values, descending      */
+  double norm2;      /* ||X||^2                                               */
+  int32_t cap;       /* largest token rank (0: none)                          */
+} jolt_alloc_cell;
+jolt_status jolt_allocate(const jolt_alloc_cell *cells, int32_t n_cells, double budget_bytes,
+                          int32_t *choice, double *lambda);
+
 /* Thread-local description of the last error of this thread ("" if none). */
 const char *jolt_last_error(void);
 

@@ -99,3 +99,33 @@ def flash_compress_cell(X, r_T, r_F, bits, factor_dtype, Pi, q_cap, oversample=1
     from .compress import residual_cell
     A, B, G = flash_st_hosvd(X, r_T, r_F, q_cap, oversample, power_iters, sketch_seed)
     return residual_cell(X, A, B, G, r_T, r_F, bits, factor_dtype, Pi)
+
+
+def flash_compress(groups, budget, factor_dtype, rotation_seed, H_q, group_start, q_cap,
+                   oversample=16, power_iters=2, sketch_seed=0):
+    """The FlashJoLT pipeline: spectra of every cell (q_cap token energies,
+    synthetic tail entry, exact feature energies), the allocator under the
+    byte budget with token ranks capped at q_cap, then each cell compressed.
+    Returns (cache, allocation)."""
+    from .allocate import CellStats, allocate
+    from .compress import compress
+    fb = 4 if factor_dtype == "f32" else 2
+    stats = []
+    for XK, XV in groups:
+        for X in (XK, XV):
+            gs, H, T, d = X.shape
+            sT2, sF2, n2 = flash_spectra(X, q_cap, oversample, power_iters, sketch_seed)
+            stats.append(CellStats(T=T, d=d, group_size=gs, H=H, factor_bytes=fb, sT2=sT2,
+                                   sF2=sF2, norm2=n2, cap=q_cap))
+    choice, _ = allocate(stats, budget)
+    alloc = [(tuple(choice[2 * g]), tuple(choice[2 * g + 1])) for g in range(len(groups))]
+    from .rotation import rotation
+    Pi = rotation(rotation_seed, groups[0][0].shape[3])
+    cells = [tuple(flash_compress_cell(X, *a, factor_dtype, Pi, q_cap, oversample, power_iters,
+                                       sketch_seed) for X, a in ((XK, aK), (XV, aV)))
+             for (XK, XV), (aK, aV) in zip(groups, alloc)]
+    XK0 = groups[0][0]
+    cache = {"T": XK0.shape[2], "H": XK0.shape[1], "H_q": H_q, "d": XK0.shape[3],
+             "n_layers": group_start[-1], "group_start": list(group_start),
+             "factor_dtype": factor_dtype, "rotation_seed": int(rotation_seed), "cells": cells}
+    return cache, alloc

@@ -153,3 +153,55 @@ def test_gpu_compressed_cache_decodes_like_oracle():
     want = att.decode_attention([cache], 0, q.astype(np.float64), [cfg.T], inv, 1 / math.sqrt(cfg.d))
     r = float(np.linalg.norm(got - want) / np.linalg.norm(want))
     assert r <= 5e-3 and float(np.max(np.abs(got - want))) <= 2e-2
+
+
+@pytest.mark.timeout(600)
+def test_gpu_pipeline_matches_oracle_pipeline():
+    """Spectra -> native allocator -> cells on the GPU (compressor.compress_cache)
+    against the oracle's FlashJoLT pipeline at 3x on two layer groups of the
+    64K stack's shape (T shortened to 4096): the same allocation table, stored
+    reconstructions within 1e-6, and the GPU decode of the GPU-built cache
+    against the oracle's decode of it."""
+    from compressed_cache_decode_jolt_amd.compressor import compress_cache
+    from oracle.compress import budget_for
+    cfg = get_config(2)
+    T, ng = 4096, 2
+    host, dev = [], []
+    for g in range(ng):
+        pair = [gen.to_bf16_values(gen.kv_group(cfg, 0, g, tau, T=T)).astype(np.float64)
+                for tau in (0, 1)]
+        host.append(tuple(pair))
+        dev.append(tuple(torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).cuda()
+                         for x in pair))
+    starts = [0, 4, 8]
+    budget = budget_for(3.0, 8, cfg.H, cfg.d, T)
+    t0 = time.perf_counter()
+    cache, alloc = compress_cache(dev, cfg.H_q, starts, budget=budget, q_cap=128, **FLASH)
+    t_gpu = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    want_cache, want_alloc = flash.flash_compress(host, budget, "bf16", 0x4A4F4C54, cfg.H_q, starts,
+                                                  128, **FLASH)
+    t_ora = time.perf_counter() - t0
+    print(f"pipeline (2 groups x 4 layers, T={T}): GPU {t_gpu:.2f} s, oracle {t_ora:.2f} s; "
+          f"allocation {alloc}")
+    assert [tuple(map(tuple, a)) for a in alloc] == [tuple(map(tuple, a)) for a in want_alloc]
+    for g in range(ng):
+        for tau in (0, 1):
+            a, b = cache["cells"][g][tau], want_cache["cells"][g][tau]
+            if a["r_T"]:
+                ra, rb = stored_recon(a), stored_recon(b)
+                assert np.linalg.norm(ra - rb) <= 1e-6 * np.linalg.norm(rb)
+    h = J.jolt_load_cache(cache)
+    inv = gen.rope_inv_freq_input(cfg.rope_base, cfg.d)
+    for layer in (0, 5):
+        q = gen.cfg_queries(cfg, 0, layer)[None]
+        qt = torch.from_numpy(q).to(torch.bfloat16).cuda()
+        out = torch.empty((1, cfg.H_q, cfg.d), dtype=torch.float32, device="cuda")
+        ws = torch.empty(J.jolt_decode_workspace_size([h], layer), dtype=torch.uint8, device="cuda")
+        J.jolt_decode_attention([h], layer, qt, [T], inv, 1 / math.sqrt(cfg.d), out, ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        want = att.decode_attention([cache], layer, q.astype(np.float64), [T], inv,
+                                    1 / math.sqrt(cfg.d))
+        assert float(np.linalg.norm(got - want) / np.linalg.norm(want)) <= 5e-3
+        assert float(np.max(np.abs(got - want))) <= 2e-2
