@@ -12,4 +12,5 @@ from ._jolt import (  # noqa: F401
     jolt_dense_workspace_size, jolt_dense_attention, jolt_make_rotation, jolt_debug_unpack, jolt_debug_sincos,
     jolt_last_error, lib, jolt_flash_spectra, jolt_flash_compress_cell, jolt_quantize_rows,
     jolt_decode_attention_noalloc, jolt_noalloc_scratch_bytes, jolt_allocate,
+    jolt_flash_layer_groups,
 )

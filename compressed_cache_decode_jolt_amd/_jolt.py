@@ -100,6 +100,11 @@ EXPORTS = {
                                                 C.POINTER(jolt_launch), C.c_void_p]),
     "jolt_allocate": (C.c_int, [C.POINTER(jolt_alloc_cell), C.c_int32, C.c_double,
                                 C.POINTER(C.c_int32), C.POINTER(C.c_double)]),
+    "jolt_flash_layer_groups": (C.c_int, [C.POINTER(C.c_void_p), C.POINTER(C.c_void_p), C.c_int,
+                                          C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                          C.POINTER(jolt_flash_params), C.c_double, C.c_int32,
+                                          C.POINTER(C.c_int32), C.POINTER(C.c_int32),
+                                          C.POINTER(C.c_double), C.c_void_p]),
     "jolt_last_error": (C.c_char_p, []),
     "jolt_make_rotation": (C.c_int, [C.c_uint64, C.c_int32, C.POINTER(C.c_double)]),
     "jolt_debug_unpack": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
@@ -520,3 +525,26 @@ def jolt_allocate(cells, budget):
     lam = C.c_double()
     _check(lib().jolt_allocate(arr, n, C.c_double(float(budget)), out, C.byref(lam)))
     return [tuple(out[3 * i:3 * i + 3]) for i in range(n)], lam.value
+
+
+def jolt_flash_layer_groups(k_layers, v_layers, r, tau, max_group=0, oversample=16,
+                            power_iters=2, sketch_seed=0, stream=None):
+    """Alignment-based grouping of consecutive layers: k_layers[l], v_layers[l]
+    device tensors [H, T, d].  Returns (group_start, alignments)."""
+    import torch
+    n = len(k_layers)
+    if n < 1 or len(v_layers) != n:
+        raise ValueError("one key and one value tensor per layer")
+    H, T, d = k_layers[0].shape
+    for t in list(k_layers) + list(v_layers):
+        _check_tensor("layer", t, (k_layers[0].dtype,), (H, T, d))
+    ks = (C.c_void_p * n)(*[t.data_ptr() for t in k_layers])
+    vs = (C.c_void_p * n)(*[t.data_ptr() for t in v_layers])
+    starts = (C.c_int32 * (n + 1))()
+    ng = C.c_int32()
+    al = (C.c_double * max(1, n - 1))()
+    P = _flash_params(r, oversample, power_iters, sketch_seed)
+    _check(lib().jolt_flash_layer_groups(ks, vs, _dtype_code(k_layers[0]), n, H, T, d,
+                                         C.byref(P), C.c_double(tau), int(max_group), starts,
+                                         C.byref(ng), al, _stream(stream)))
+    return list(starts[:ng.value + 1]), list(al[:n - 1])

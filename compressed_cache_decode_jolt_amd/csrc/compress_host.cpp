@@ -460,6 +460,80 @@ extern "C" jolt_status jolt_flash_compress_cell(
   return set_error(JOLT_OK, "");
 }
 
+// Alignment-based layer grouping ("A JoLT for the KV cache" §3): each
+// layer's token basis U_l (T x r) from the randomized SVD of its keys and
+// values side by side, the alignment ||U_l^T U_{l+1}||_F^2 / r of neighbours,
+// and groups = maximal runs of neighbours aligned at least tau (at most
+// max_group layers each, 0 = no limit).
+extern "C" jolt_status jolt_flash_layer_groups(const void *const *k_layers,
+                                               const void *const *v_layers, jolt_dtype x_dtype,
+                                               int32_t n_layers, int32_t n_kv_heads, int32_t T,
+                                               int32_t head_dim, const jolt_flash_params *p,
+                                               double tau, int32_t max_group,
+                                               int32_t *group_start, int32_t *n_groups,
+                                               double *align, jolt_stream stream) {
+  std::string why;
+  if (!k_layers || !v_layers || !group_start || !n_groups || n_layers < 1 || max_group < 0)
+    return set_error(JOLT_E_INVALID, "jolt_flash_layer_groups: bad arguments");
+  for (int l = 0; l < n_layers; ++l)
+    if (!check_shape(k_layers[l], x_dtype, 2, n_kv_heads, T, head_dim, p, &why) || !v_layers[l])
+      return set_error(JOLT_E_INVALID, "jolt_flash_layer_groups: layer %d: %s", l,
+                       why.empty() ? "NULL values" : why.c_str());
+  Ctx cx;
+  cx.s = (hipStream_t)stream;
+  if (rocblas_create_handle(&cx.h) != rocblas_status_success)
+    return set_error(JOLT_E_HIP, "rocblas_create_handle failed");
+  rocblas_set_stream(cx.h, cx.s);
+  const int eb = x_dtype == JOLT_F32 ? 4 : 2;
+  const size_t half = (size_t)n_kv_heads * T * head_dim * eb;
+  const Shape sh{2, n_kv_heads, T, head_dim, x_dtype == JOLT_F32 ? 1 : 2};
+  std::vector<double> a(n_layers > 1 ? n_layers - 1 : 0);
+  auto run = [&]() -> bool {
+    DevMem dX, dC, prevU;
+    int prev_q = 0;
+    if (!dalloc(cx, dX, 2 * half)) return false;
+    for (int l = 0; l < n_layers; ++l) {
+      // keys then values of the layer, contiguous: [2][H][T][d]
+      CK(hipMemcpyAsync(dX.p, k_layers[l], half, hipMemcpyDeviceToDevice, cx.s));
+      CK(hipMemcpyAsync((uint8_t *)dX.p + half, v_layers[l], half, hipMemcpyDeviceToDevice, cx.s));
+      DevMem U;
+      int q = 0;
+      std::vector<double> sig;
+      if (!token_basis(cx, sh, dX.p, *p, U, &q, sig)) return false;
+      if (l > 0) {
+        if (!dC.p && !dalloc(cx, dC, sizeof(double) * q * q)) return false;
+        GemmOp g;
+        g.A = prevU.p, g.a_i = 1, g.a_k = prev_q;
+        g.B = U.p, g.b_k = q, g.b_j = 1;
+        g.C = dC.get<double>(), g.c_i = q, g.c_j = 1;
+        g.M = prev_q, g.N = q, g.K = T;
+        if (!gemm(cx, g)) return false;
+        std::vector<double> hc((size_t)prev_q * q);
+        CK(hipMemcpyAsync(hc.data(), dC.p, sizeof(double) * hc.size(), hipMemcpyDeviceToHost, cx.s));
+        CK(hipStreamSynchronize(cx.s));
+        double ss = 0.0;
+        for (double v : hc) ss += v * v;
+        a[l - 1] = ss / prev_q;
+      }
+      std::swap(prevU.p, U.p);
+      prev_q = q;
+    }
+    return true;
+  };
+  if (!run()) return set_error(JOLT_E_HIP, "jolt_flash_layer_groups: %s", cx.err.c_str());
+  int ng = 0;
+  group_start[0] = 0;
+  for (int l = 1; l < n_layers; ++l) {
+    const int size = l - group_start[ng];
+    if (a[l - 1] < tau || (max_group > 0 && size >= max_group)) group_start[++ng] = l;
+  }
+  group_start[++ng] = n_layers;
+  *n_groups = ng;
+  if (align)
+    for (int l = 0; l + 1 < n_layers; ++l) align[l] = a[l];
+  return set_error(JOLT_OK, "");
+}
+
 extern "C" jolt_status jolt_quantize_rows(const double *rows, int64_t n_rows, int32_t d, int32_t bits,
                                           uint8_t *codes, float *scales, jolt_stream stream) {
   if (n_rows < 0 || d < 2 || d > 128 || (bits != 2 && bits != 4 && bits != 8) || (d * bits) % 8)

@@ -278,6 +278,23 @@ jolt_status jolt_flash_compress_cell(const void *X, jolt_dtype x_dtype, int32_t 
                                      jolt_dtype factor_dtype, void *A, void *B, void *G,
                                      uint8_t *codes, float *scales, jolt_stream stream);
 
+/* Alignment-based layer grouping (the summary's §3: consecutive layers whose
+ * token-mode singular vectors align share a group, computed from the cache
+ * itself).  k_layers[l], v_layers[l]: DEVICE [n_kv_heads][T][head_dim] of
+ * layer l in x_dtype.  Each layer's basis is the leading q_cap left singular
+ * vectors of its keys and values side by side (params as above); the
+ * alignment of neighbours is ||U_l^T U_(l+1)||_F^2 / q_cap; groups are the
+ * maximal runs of neighbours aligned at least tau, split to at most
+ * max_group layers (0: no limit).  HOST group_start[n_layers + 1] receives
+ * 0 = g_0 < ... < g_n = n_layers, *n_groups = n, HOST align[n_layers - 1]
+ * (may be NULL) the alignments.  Synchronous.  Errors: JOLT_E_INVALID,
+ * JOLT_E_HIP. */
+jolt_status jolt_flash_layer_groups(const void *const *k_layers, const void *const *v_layers,
+                                    jolt_dtype x_dtype, int32_t n_layers, int32_t n_kv_heads,
+                                    int32_t T, int32_t head_dim, const jolt_flash_params *params,
+                                    double tau, int32_t max_group, int32_t *group_start,
+                                    int32_t *n_groups, double *align, jolt_stream stream);
+
 /* The quantiser and packer alone, on rotated residual rows: DEVICE rows
  * [n_rows][d] float64 -> DEVICE codes [n_rows][d*bits/8] and scales [n_rows]:
  * delta = fl32(2 max|r| / (2^b - 1)), c = clip(rint(r / delta + (2^b - 1)/2))
