@@ -272,19 +272,18 @@ struct Plan {
 // hg1: one query per KV head.  The classes launched as HG1 variants (value
 // ranks above 128, or key ranks above 256) park 4 lanes' worth of each value
 // block per wave instead of 64, and with key ranks up to 256 run 8 waves.
+// The size is taken per sequence, with the waves and variant its own ranks
+// select; a launch class that runs a sequence with fewer waves or as the
+// HG1 variant (a batch mixing value ranks) uses no more LDS for it.
 static int mfma_lds_bytes(const CellDev &k, const CellDev &v, int d, bool hg1) {
   // key ranks above 256 keep Pi in registers (4 waves), not in LDS
   const bool wide = k.rT_pad > 8 * kRankPad;
-  const int kpath = 2 * d * (k.rT_pad + kRowPad) + (k.bits > 0 && !wide ? 2 * d * (d + kRowPad) : 0);
+  const bool pi_lds = k.bits > 0 && !wide;
   const bool big_v = v.rT_pad / 16 > 8;
   // launched as an HG1 variant
   const bool hg1v = hg1 && hg1_variant(k.bits, v.bits, k.rT_pad / kRankPad, v.rT_pad / 16);
   const int waves = wide || (big_v && !hg1v) ? 4 : 8;
-  // fp16 value partials of every wave
-  const int park = waves * (v.rT_pad / 16 + 8) * (hg1v ? 32 : 512);
-  // + softmax reduction, frequencies (and / 2 pi), query operands, combined
-  // value tiles and the token-block counter
-  return std::max(kpath, park) + 1024 + 512 + 6144 + 1024 * (v.rT_pad / 16 + 8) + 16;
+  return (int)mfma_lds_layout(d, k.rT_pad / kRankPad, pi_lds, v.rT_pad / 16, waves, hg1v).total;
 }
 
 static bool mfma_ok(const jolt_cache *c, int layer, int *lds) {

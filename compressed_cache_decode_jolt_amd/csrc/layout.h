@@ -97,6 +97,40 @@ JOLT_HD inline void vcode_pos(int h, int t, int f, int bits, int T_pad, int d, s
 
 // Padded rank of a cell: multiples of 32; ranks above 256 pad to 64, so wide
 // key tiles take an even number of 32-rank MFMA steps.
+// LDS of one MFMA decode workgroup, byte offsets into its dynamic LDS.  The
+// host sizes the launch with .total and the kernel places its arrays at these
+// offsets, so the two cannot disagree.
+//   kt: key-rank blocks of 32; nmv: value-rank blocks of 16; pi_lds: Pi's
+//   fp16 image sits in LDS next to W2_K; hg1v: the one-query-per-KV-head
+//   kernel variant (parks 4 lanes' f16x4 per value block instead of 64).
+// During the token-block loop: W2_K (+ Pi) at [0, kpath), the softmax (m, l)
+// exchange, the frequencies, the query operands (and their low halves with
+// more than 8 queries per KV head) and the block counter.  After it the
+// parked value partials take [0, park) and the combined value tiles Xa / Xc
+// go behind them when they fit below kpath (one-query variant only), else
+// behind the query operands.
+struct MfmaLds {
+  uint32_t kpath, park, red, ifr, qf, ql, xa, xa_bytes, ctr, total;
+  bool xa_r0;
+};
+JOLT_HD constexpr MfmaLds mfma_lds_layout(int d, int kt, bool pi_lds, int nmv, int waves,
+                                          bool hg1v) {
+  MfmaLds l{};
+  l.kpath = 2u * d * (32 * kt + kRowPad) + (pi_lds ? 2u * d * (d + kRowPad) : 0u);
+  l.park = (uint32_t)waves * (nmv + 8) * (hg1v ? 4 : 64) * 8;
+  l.xa_bytes = (uint32_t)(nmv + 8) * 64 * 16;
+  l.xa_r0 = hg1v && l.park + l.xa_bytes <= l.kpath;
+  l.red = l.xa_r0 || l.kpath > l.park ? l.kpath : l.park;
+  l.ifr = l.red + 2u * 16 * waves * 4;   // [2][waves][16] floats
+  l.qf = l.ifr + 2u * 64 * 4;            // [2][64] floats
+  l.ql = l.qf + 4u * 96 * 16;            // [4 K-steps][16][6] f16x8
+  l.xa = l.xa_r0 ? l.park : l.ql;        // low halves alias Xa: Xa is written after the loop
+  // the counter is live during the loop: never inside [0, kpath) or Ql
+  l.ctr = l.xa_r0 ? l.ql : l.xa + l.xa_bytes;
+  l.total = l.ctr + 16;
+  return l;
+}
+
 inline int pad_rank(int r) {
   const int m = r > 8 * kRankPad ? 2 * kRankPad : kRankPad;
   return (r + m - 1) / m * m;

@@ -250,6 +250,46 @@ static void run_case(int T, int H, int d, const std::vector<int> &gsz,
   std::printf("case T=%d H=%d groups=%d: %d failures so far\n", T, H, ng, fails);
 }
 
+// The MFMA decode kernel's LDS layout (mfma_lds_layout, shared by the host's
+// launch size and the kernel): for every launch class, the arrays live during
+// the token-block loop are pairwise disjoint, so are those live after it, and
+// all end within the size the host requests.
+static void check_mfma_lds() {
+  struct R { uint32_t b, e; };
+  auto disjoint = [](R x, R y) { return x.e <= y.b || y.e <= x.b || x.b == x.e || y.b == y.e; };
+  const int kts[] = {0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16};
+  int n = 0;
+  for (int kt : kts)
+    for (int pi = 0; pi < 2; ++pi)
+      for (int nmv = 0; nmv <= 32; ++nmv)
+        for (int waves = 4; waves <= 8; waves += 4)
+          for (int hg1 = 0; hg1 < 2; ++hg1) {
+            const jolt::MfmaLds L = jolt::mfma_lds_layout(128, kt, pi, nmv, waves, hg1);
+            const R kp{0, L.kpath}, red{L.red, L.red + 128u * waves}, ifr{L.ifr, L.ifr + 512},
+                qf{L.qf, L.qf + 6144}, ql{L.ql, hg1 ? L.ql : L.ql + 6144}, ctr{L.ctr, L.ctr + 4},
+                park{0, L.park}, xa{L.xa, L.xa + L.xa_bytes};
+            const R loop[] = {kp, red, ifr, qf, ql, ctr};
+            const R after[] = {park, xa, red, ifr, qf, ctr};
+            for (int i = 0; i < 6; ++i)
+              for (int j = i + 1; j < 6; ++j) {
+                CHECK(disjoint(loop[i], loop[j]), "LDS loop regions %d/%d overlap (kt%d pi%d nmv%d w%d hg1 %d)",
+                      i, j, kt, pi, nmv, waves, hg1);
+                CHECK(disjoint(after[i], after[j]), "LDS post-loop regions %d/%d overlap (kt%d pi%d nmv%d w%d hg1 %d)",
+                      i, j, kt, pi, nmv, waves, hg1);
+              }
+            for (const R &r : loop) CHECK(r.e <= L.total, "LDS region past the launch size (kt%d nmv%d)", kt, nmv);
+            for (const R &r : after) CHECK(r.e <= L.total, "LDS region past the launch size (kt%d nmv%d)", kt, nmv);
+            CHECK(L.total % 4 == 0 && L.ctr % 4 == 0 && L.xa % 16 == 0 && L.qf % 16 == 0, "LDS alignment");
+            // a sequence launched with fewer waves or as the one-query variant
+            // needs no more LDS than the host's per-sequence size
+            CHECK(jolt::mfma_lds_layout(128, kt, pi, nmv, 4, hg1).total <= jolt::mfma_lds_layout(128, kt, pi, nmv, waves, hg1).total &&
+                      jolt::mfma_lds_layout(128, kt, pi, nmv, waves, true).total <= jolt::mfma_lds_layout(128, kt, pi, nmv, waves, hg1).total,
+                  "LDS size not monotone (kt%d nmv%d)", kt, nmv);
+            ++n;
+          }
+  std::printf("mfma LDS layouts: %d classes checked, %d failures so far\n", n, fails);
+}
+
 int main() {
   const int d = 128;
   // (T, H, group sizes, allocation)
@@ -258,6 +298,7 @@ int main() {
   run_case(1, 3, d, {1}, {1, 16, 4, 1, 16, 8});
   run_case(1111, 2, d, {3}, {512, 96, 4, 300, 64, 2});
   run_case(130, 2, d, {1}, {0, 0, 8, 0, 0, 4});
+  check_mfma_lds();
   if (fails) {
     std::printf("layout check FAILED (%d)\n", fails);
     return 1;
