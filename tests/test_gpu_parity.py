@@ -475,6 +475,27 @@ def test_one_query_two_blocks_per_step(split):
         assert np.max(np.abs(got[b] - want[b])) <= 2e-2
 
 
+@pytest.mark.parametrize("split", [256, 1024])
+def test_one_query_wide_keys_long_splits(split):
+    """One query per KV head with key ranks above 256 (4 waves, Pi's
+    fragments in registers) over long splits: ragged lengths, residual-free
+    and 2/4/8-bit keys, the three value classes."""
+    d, H, H_q = 128, 4, 4
+    spec = [(1111, (320, 64, 2), (160, 64, 8)), (1500, (384, 96, 8), (96, 32, 4)),
+            (700, (448, 64, 0), (200, 64, 8)), (999, (512, 64, 0), (64, 32, 2)),
+            (1300, (352, 64, 4), (256, 96, 4))]
+    caches = [gen.small_cache(170 + i, T, H, H_q, d, [(aK, aV)], [1])
+              for i, (T, aK, aV) in enumerate(spec)]
+    inv = gen.rope_inv_freq_input(1e4, d)
+    q = np.stack([gen.queries(171, i, 0, H_q, d, "bf16") for i in range(len(spec))])
+    q_pos = [T for T, _, _ in spec]
+    got = run_decode(caches, 0, q, q_pos, inv, 0.088, kernel=J.KERNEL_MFMA, split=split)
+    want = oracle_decode(caches, 0, q, q_pos, inv, 0.088)
+    for b in range(len(spec)):
+        assert rel_l2(got[b], want[b]) <= 5e-3, (b, rel_l2(got[b], want[b]))
+        assert np.max(np.abs(got[b] - want[b])) <= 2e-2
+
+
 DET_CASES = [(2, 8, 1500, (64, 32, 4), (48, 32, 2), 512),     # 8 waves, two blocks per step
              (2, 8, 2000, (96, 64, 8), (96, 64, 4), 0),       # 8 waves, value ranks <= 128
              (4, 4, 1300, (320, 64, 2), (160, 64, 8), 256),   # one query, wide keys, 4 waves
