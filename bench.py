@@ -406,7 +406,7 @@ def main():
         achieved = bytes_launch / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                 "frac": achieved / (PEAK_HBM / 1e9)}
-    roof["traffic"] = measured_traffic(cfg.name, kname)
+    roof["traffic"] = measured_traffic(f"{cfg.name}@{ratio_key}", kname)
     roof["kernel_ms"] = kern_ms
     roof["alg_bytes_per_launch"] = bytes_launch
     roof["alg_flops_per_launch"] = flops_launch

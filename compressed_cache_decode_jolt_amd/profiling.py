@@ -2,14 +2,19 @@
 
     python -m compressed_cache_decode_jolt_amd.profiling stats CSV --command CMD --out FILE
     python -m compressed_cache_decode_jolt_amd.profiling traffic --workload NAME --kernel SUBSTR \\
-        --fetch CSV --write CSV --calib-fetch CSV --calib-write CSV --copy-bytes N --out JSON
+        --fetch CSV --write CSV --calib-fetch CSV --calib-write CSV --copy-bytes N --out JSON \\
+        [--md FILE --command CMD --title T --alg-bytes B]
+    python -m compressed_cache_decode_jolt_amd.profiling counters CSV --kernel SUBSTR \\
+        --command CMD --out FILE
 
 `stats` turns a `rocprofv3 --kernel-trace --stats -f csv` kernel_stats.csv
 into a short markdown table.  `traffic` turns two `--pmc` runs (FETCH_SIZE,
 then WRITE_SIZE, KiB per dispatch) into HBM bytes per launch of one kernel,
 each counter scaled by what it reads for a plain device copy of known size
 (the calibration runs), and records the hash of the kernel sources so a
-stale figure is never reported for a changed kernel.
+stale figure is never reported for a changed kernel.  `counters` turns one
+`--pmc` run of busy / activity counters into a per-kernel table of means per
+dispatch with the derived utilisation ratios.
 """
 import argparse
 import csv
@@ -111,6 +116,63 @@ def traffic(args):
     data[f"{args.workload}/{args.name or args.kernel}"] = rec
     json.dump(data, open(args.out, "w"), indent=1, sort_keys=True)
     print(json.dumps(rec, indent=1))
+    if getattr(args, "md", None):
+        lines = [f"# {args.title}", "", "Commands (from the repository root on one MI355X):", "",
+                 "```", args.command, "```", "",
+                 "| quantity | value |", "|---|---|",
+                 "| copy of %s B: FETCH_SIZE | %s (=> %.1f B per unit) |" % (
+                     f"{args.copy_bytes:,}", f"{fraw:,.0f}", ff),
+                 "| copy of %s B: WRITE_SIZE | %s (=> %.1f B per unit) |" % (
+                     f"{args.copy_bytes:,}", f"{wraw:,.0f}", wf),
+                 "| `%s` FETCH_SIZE x factor | %s B per launch (mean of %d dispatches) |" % (
+                     args.kernel, f"{fb:,.0f}", len(fv)),
+                 "| `%s` WRITE_SIZE x factor | %s B per launch (mean of %d dispatches) |" % (
+                     args.kernel, f"{wb:,.0f}", len(wv)),
+                 "| HBM traffic per launch | %s B |" % f"{fb + wb:,.0f}"]
+        if args.alg_bytes:
+            lines += ["| algorithmic bytes per launch | %s B |" % f"{args.alg_bytes:,.0f}",
+                      "| traffic / algorithmic | %.2f |" % ((fb + wb) / args.alg_bytes)]
+        lines += ["", "Per kernel instantiation (mean per dispatch):", "",
+                  "| kernel | dispatches | fetch B | write B |", "|---|---|---|---|"]
+        for name in sorted(fetch):
+            f_ = fetch[name]
+            w_ = write.get(name, [0.0])
+            lines.append("| `%s` | %d | %s | %s |" % (short_name(name), len(f_),
+                                                    f"{ff * sum(f_) / len(f_):,.0f}",
+                                                    f"{wf * sum(w_) / len(w_):,.0f}"))
+        lines += ["", "Kernel sources hash: `%s`" % rec["kernel_hash"], ""]
+        open(args.md, "w").write("\n".join(lines))
+
+
+# derived ratios of the busy counters: (name, numerator, denominator)
+RATIOS = [("MFMA busy / CU busy", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES"),
+          ("VALU active / wave cycles", "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES"),
+          ("LDS active / wave cycles", "SQ_ACTIVE_INST_LDS", "SQ_WAVE_CYCLES"),
+          ("waiting / wave cycles", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
+          ("waiting on LDS / wave cycles", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES")]
+
+
+def counters_table(path, match):
+    """Markdown table: per kernel whose name contains ``match``, the mean per
+    dispatch of every counter in a --pmc CSV, then the ratios of RATIOS whose
+    counters are present."""
+    names = []
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] not in names:
+            names.append(r["Counter_Name"])
+    per = {c: counter_per_dispatch(path, c, match) for c in names}
+    kernels = sorted({k for c in names for k in per[c]})
+    mean = {k: {c: sum(per[c][k]) / len(per[c][k]) for c in names if k in per[c]} for k in kernels}
+    ratios = [r for r in RATIOS if r[1] in names and r[2] in names]
+    head = ["kernel", "dispatches"] + names + [r[0] for r in ratios]
+    out = ["| " + " | ".join(head) + " |", "|" + "---|" * len(head)]
+    for k in kernels:
+        m = mean[k]
+        cells = ["`%s`" % short_name(k), str(len(per[names[0]].get(k, [])))]
+        cells += ["%.4g" % m[c] if c in m else "" for c in names]
+        cells += ["%.3f" % (m[n] / m[d]) if m.get(d) else "" for _, n, d in ratios]
+        out.append("| " + " | ".join(cells) + " |")
+    return "\n".join(out)
 
 
 def main():
@@ -130,6 +192,17 @@ def main():
         t.add_argument("--" + k.replace("_", "-"), required=True)
     t.add_argument("--name", default=None)
     t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--md", default=None, help="also write a markdown summary here")
+    t.add_argument("--command", default="")
+    t.add_argument("--title", default="HBM traffic")
+    t.add_argument("--alg-bytes", type=float, default=0.0)
+    c = sub.add_parser("counters")
+    c.add_argument("csv")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--command", required=True)
+    c.add_argument("--title", default="rocprofv3 counters")
+    c.add_argument("--note", default="")
+    c.add_argument("--out", required=True)
     a = ap.parse_args()
     if a.cmd == "stats":
         text = f"# {a.title}\n\nCommand (from the repository root on one MI355X):\n\n```\n{a.command}\n```\n\n"
@@ -140,6 +213,14 @@ def main():
             k, st, n = a.window[0], int(a.window[1]), int(a.window[2])
             text += ("\nMean duration of `%s` dispatches %d-%d (in start order): %.2f us\n"
                      % (k, st, st + n - 1, window_mean(a.trace, k, st, n)))
+        text += "\nKernel sources hash: `%s`\n" % kernel_hash()
+        open(a.out, "w").write(text)
+        print(text)
+    elif a.cmd == "counters":
+        text = f"# {a.title}\n\nCommand (from the repository root on one MI355X):\n\n```\n{a.command}\n```\n\n"
+        if a.note:
+            text += a.note + "\n\n"
+        text += counters_table(a.csv, a.kernel) + "\n"
         text += "\nKernel sources hash: `%s`\n" % kernel_hash()
         open(a.out, "w").write(text)
         print(text)

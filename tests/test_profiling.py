@@ -59,3 +59,17 @@ def test_kernel_hash_is_stable():
     h = P.kernel_hash()
     assert len(h) == 16 and int(h, 16) >= 0
     assert P.kernel_hash() == h
+
+
+def test_counters_table_means_per_dispatch_and_ratios(tmp_path):
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    rows = [(1, "decode_mfma<a>", "SQ_BUSY_CU_CYCLES", 100), (1, "decode_mfma<a>", "SQ_BUSY_CU_CYCLES", 100),
+            (1, "decode_mfma<a>", "SQ_VALU_MFMA_BUSY_CYCLES", 50),
+            (2, "decode_mfma<a>", "SQ_BUSY_CU_CYCLES", 400), (2, "decode_mfma<a>", "SQ_VALU_MFMA_BUSY_CYCLES", 250),
+            (3, "merge", "SQ_BUSY_CU_CYCLES", 7), (3, "merge", "SQ_VALU_MFMA_BUSY_CYCLES", 7)]
+    p = _write(tmp_path / "pmc.csv", hdr, rows)
+    t = P.counters_table(p, "decode_mfma").splitlines()
+    assert len(t) == 3 and "merge" not in "\n".join(t)
+    cells = [c.strip() for c in t[2].strip("|").split("|")]
+    # busy: (200 + 400) / 2 = 300; mfma: (50 + 250) / 2 = 150; ratio 0.5
+    assert cells[1] == "2" and cells[2] == "300" and cells[3] == "150" and cells[4] == "0.500"
