@@ -519,7 +519,6 @@ static jolt_status decode_impl(const jolt_cache *const *caches, int32_t batch, i
       ma.ws_splits = ws_splits;
       ma.split_tokens = a.split_tokens;
       ma.stride = a.stride;
-      ma.grid8 = (a.n_split & 7) == 0;
       ma.fixed_blocks = launch && launch->deterministic ? 1 : 0;
       bool done[kMaxBatchPerLaunch] = {};
       int last_class = 0;  // first member of the chunk's last launch class
@@ -561,6 +560,8 @@ static jolt_status decode_impl(const jolt_cache *const *caches, int32_t batch, i
         }
         ma.nseq = n;
         ma.rV_max = rv;
+        // XCD-aware grid (all heads of a (sequence, split) unit on one XCD)
+        ma.grid8 = (a.n_split & 7) == 0 ? 1 : ((n * a.n_split) & 7) == 0 ? 2 : 0;
         // frequency blocks of 16 whose angles stay below kRopeSmall for every
         // cached position of the launch's sequences
         int t_max = 0;

@@ -51,3 +51,36 @@ def test_old_prologue_would_overrun():
     t0 = (T // split) * split
     assert t0 + 16 * NB * (waves - 1) + 16 * NB - 1 >= T_pad
     assert max(touched_rows(T, split, NB, waves)[1]) < T_pad
+
+
+@pytest.mark.parametrize("H,n_split,nseq", [(32, 1, 16), (8, 4, 2), (8, 8, 3), (4, 2, 12), (2, 16, 1),
+                                            (32, 3, 8)])
+def test_xcd_grids_cover_every_unit_once(H, n_split, nseq):
+    """The MFMA kernel's block -> (head, split, sequence) maps: every work item
+    exactly once, in range, and with an XCD-aware grid all heads of one
+    (sequence, split) unit on one XCD (workgroups go to XCD linear id mod 8)."""
+    mode = 1 if n_split % 8 == 0 else 2 if (nseq * n_split) % 8 == 0 else 0
+    if mode == 1:
+        grid = (8 * H, n_split // 8, nseq)
+    elif mode == 2:
+        grid = (8 * H, nseq * n_split // 8, 1)
+    else:
+        grid = (H, n_split, nseq)
+    seen, xcd_of = set(), {}
+    for z in range(grid[2]):
+        for y in range(grid[1]):
+            for x in range(grid[0]):
+                lin = x + grid[0] * (y + grid[1] * z)
+                if mode == 1:
+                    b, h, split = z, x >> 3, y * 8 + (x & 7)
+                elif mode == 2:
+                    h, u = x >> 3, y * 8 + (x & 7)
+                    b, split = u // n_split, u % n_split
+                else:
+                    b, h, split = z, x, y
+                assert 0 <= b < nseq and 0 <= h < H and 0 <= split < n_split
+                seen.add((b, h, split))
+                xcd_of.setdefault((b, split), set()).add(lin % 8)
+    assert len(seen) == H * n_split * nseq
+    if mode:
+        assert all(len(v) == 1 for v in xcd_of.values())
