@@ -256,6 +256,8 @@ def main():
                     help="device copies of the caches rotated over the steps (default: enough "
                          "that a step reads HBM, not the Infinity Cache)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--deterministic", action="store_true",
+                    help="fixed token-block schedule (bitwise repeatable outputs)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
@@ -330,7 +332,8 @@ def main():
         for l in range(L):
             e = (evb[(i * L + l) % n_ev], eve[(i * L + l) % n_ev]) if timed else None
             J.jolt_decode_attention(cs, l, qs[l], q_pos, inv, scale, out, ws, kernel=kernel,
-                                    split_tokens=split, stream=st, events=e)
+                                    split_tokens=split, stream=st, events=e,
+                                    deterministic=args.deterministic)
 
     def timed_steps(run):
         """Warm-up steps, then exactly args.steps steps between two events."""
@@ -461,6 +464,7 @@ def main():
                    "head_dim": d, "T": T, "budget": ratio_key,
                    "allocation": [list(map(list, a)) for a in alloc[:1]] if L == 1 else ratio_key,
                    "kernel": args.kernel, "split_tokens": split, "cache_copies": copies,
+                   "schedule": "fixed" if args.deterministic else "on-demand",
                    "step_alg_bytes": step_bytes},
         "timing": {"eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
                    "reported": "graph" if graph_ms is not None else "eager"},

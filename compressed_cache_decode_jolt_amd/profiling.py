@@ -104,10 +104,12 @@ def traffic(args):
     assert fetch and write, f"no dispatch of a kernel matching {args.kernel!r}"
     fv = [x for v in fetch.values() for x in v]
     wv = [x for v in write.values() for x in v]
-    fb, wb = ff * sum(fv) / len(fv), wf * sum(wv) / len(wv)
+    # a launch (one layer call) may run several launch classes, i.e. dispatches
+    per = getattr(args, "dispatches_per_launch", 1.0) or 1.0
+    fb, wb = per * ff * sum(fv) / len(fv), per * wf * sum(wv) / len(wv)
     rec = {"kernel_hash": kernel_hash(), "bytes_per_launch": fb + wb,
            "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
-           "dispatches": [len(fv), len(wv)],
+           "dispatches": [len(fv), len(wv)], "dispatches_per_launch": per,
            "calibration": {"copy_bytes": args.copy_bytes, "fetch_counter": fraw,
                            "write_counter": wraw, "fetch_bytes_per_unit": ff,
                            "write_bytes_per_unit": wf},
@@ -124,10 +126,10 @@ def traffic(args):
                      f"{args.copy_bytes:,}", f"{fraw:,.0f}", ff),
                  "| copy of %s B: WRITE_SIZE | %s (=> %.1f B per unit) |" % (
                      f"{args.copy_bytes:,}", f"{wraw:,.0f}", wf),
-                 "| `%s` FETCH_SIZE x factor | %s B per launch (mean of %d dispatches) |" % (
-                     args.kernel, f"{fb:,.0f}", len(fv)),
-                 "| `%s` WRITE_SIZE x factor | %s B per launch (mean of %d dispatches) |" % (
-                     args.kernel, f"{wb:,.0f}", len(wv)),
+                 "| `%s` FETCH_SIZE x factor | %s B per launch (%d dispatches, %.3g per launch) |" % (
+                     args.kernel, f"{fb:,.0f}", len(fv), per),
+                 "| `%s` WRITE_SIZE x factor | %s B per launch (%d dispatches, %.3g per launch) |" % (
+                     args.kernel, f"{wb:,.0f}", len(wv), per),
                  "| HBM traffic per launch | %s B |" % f"{fb + wb:,.0f}"]
         if args.alg_bytes:
             lines += ["| algorithmic bytes per launch | %s B |" % f"{args.alg_bytes:,.0f}",
@@ -184,6 +186,7 @@ def main():
     s.add_argument("--title", default="rocprofv3 kernel statistics")
     s.add_argument("--note", default="")
     s.add_argument("--out", required=True)
+    s.add_argument("--top", type=int, default=8, help="rows of the table")
     s.add_argument("--trace", default=None, help="kernel-trace CSV for --window")
     s.add_argument("--window", nargs=3, metavar=("KERNEL", "START", "COUNT"), default=None,
                    help="also report the mean duration of these dispatches of KERNEL")
@@ -196,6 +199,8 @@ def main():
     t.add_argument("--command", default="")
     t.add_argument("--title", default="HBM traffic")
     t.add_argument("--alg-bytes", type=float, default=0.0)
+    t.add_argument("--dispatches-per-launch", type=float, default=1.0,
+                   help="kernel dispatches per launch of the bench's roofline (a layer call)")
     c = sub.add_parser("counters")
     c.add_argument("csv")
     c.add_argument("--kernel", required=True)
@@ -208,7 +213,7 @@ def main():
         text = f"# {a.title}\n\nCommand (from the repository root on one MI355X):\n\n```\n{a.command}\n```\n\n"
         if a.note:
             text += a.note + "\n\n"
-        text += stats_table(a.csv) + "\n"
+        text += stats_table(a.csv, a.top) + "\n"
         if a.window:
             k, st, n = a.window[0], int(a.window[1]), int(a.window[2])
             text += ("\nMean duration of `%s` dispatches %d-%d (in start order): %.2f us\n"
