@@ -427,10 +427,16 @@ def jolt_debug_unpack(cache, layer, tau, stream=None):
 
 
 def jolt_debug_sincos(angles, variant=0):
+    """variant 0/1: angles [n]; variant 2: (position, inv_freq) pairs [n, 2]."""
     x = np.ascontiguousarray(angles, dtype=np.float32)
-    sn, cs = np.empty_like(x), np.empty_like(x)
-    _check(lib().jolt_debug_sincos(x.ctypes.data, x.size, sn.ctypes.data, cs.ctypes.data,
-                                   int(variant)))
+    if variant == 2:
+        if x.ndim != 2 or x.shape[1] != 2:
+            raise ValueError("variant 2 takes (position, inv_freq) pairs of shape [n, 2]")
+        n = x.shape[0]
+    else:
+        n = x.size
+    sn, cs = np.empty(n, np.float32), np.empty(n, np.float32)
+    _check(lib().jolt_debug_sincos(x.ctypes.data, n, sn.ctypes.data, cs.ctypes.data, int(variant)))
     return sn, cs
 
 

@@ -832,17 +832,23 @@ extern "C" jolt_status jolt_debug_sincos(const float *angles, int32_t n, float *
                                          float *cos_out, int32_t variant) {
   if (n < 0 || (n > 0 && (!angles || !sin_out || !cos_out)))
     return fail(JOLT_E_INVALID, "NULL argument or n < 0");
-  if (variant != 0 && variant != 1) return fail(JOLT_E_INVALID, "variant %d not 0 or 1", variant);
-  for (int i = 0; i < n; ++i)
-    if (!(std::fabs(angles[i]) < (float)kMaxPos))
-      return fail(JOLT_E_INVALID, "angle %g outside (-2^20, 2^20)", (double)angles[i]);
+  if (variant < 0 || variant > 2) return fail(JOLT_E_INVALID, "variant %d not 0, 1 or 2", variant);
+  const size_t nin = (size_t)n * (variant == 2 ? 2 : 1);  // input floats
+  for (size_t i = 0; i < nin; ++i) {
+    if (variant == 2 && (i & 1)) {
+      if (!(angles[i] >= 0.0f && angles[i] <= 1.0f))
+        return fail(JOLT_E_INVALID, "inv_freq %g outside [0, 1]", (double)angles[i]);
+    } else if (!(std::fabs(angles[i]) < (float)kMaxPos)) {
+      return fail(JOLT_E_INVALID, "angle or position %g outside (-2^20, 2^20)", (double)angles[i]);
+    }
+  }
   if (n == 0) return ok();
   float *d = nullptr;
-  HIP_TRY(hipMalloc(&d, sizeof(float) * 3 * (size_t)n));
-  hipError_t e = hipMemcpy(d, angles, sizeof(float) * n, hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = jolt_launch_sincos(d, n, d + n, d + 2 * (size_t)n, variant, nullptr);
-  if (e == hipSuccess) e = hipMemcpy(sin_out, d + n, sizeof(float) * n, hipMemcpyDeviceToHost);
-  if (e == hipSuccess) e = hipMemcpy(cos_out, d + 2 * (size_t)n, sizeof(float) * n, hipMemcpyDeviceToHost);
+  HIP_TRY(hipMalloc(&d, sizeof(float) * (nin + 2 * (size_t)n)));
+  hipError_t e = hipMemcpy(d, angles, sizeof(float) * nin, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = jolt_launch_sincos(d, n, d + nin, d + nin + n, variant, nullptr);
+  if (e == hipSuccess) e = hipMemcpy(sin_out, d + nin, sizeof(float) * n, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(cos_out, d + nin + n, sizeof(float) * n, hipMemcpyDeviceToHost);
   hipFree(d);
   if (e != hipSuccess) return fail(JOLT_E_HIP, "debug sincos: %s", hipGetErrorString(e));
   return ok();

@@ -763,6 +763,8 @@ __global__ void sincos_kernel(const float *x, int n, float *sn, float *cs, int v
   if (i < n) {
     if (variant == 1)
       hw_sincos(x[i], sn + i, cs + i);
+    else if (variant == 2)  // (position, inv_freq) pairs, as the key path's small-angle blocks
+      rope_rev_cs_hw(x[2 * i], x[2 * i + 1] * kInv2Pi, cs + i, sn + i);
     else
       fast_sincos(x[i], sn + i, cs + i);
   }

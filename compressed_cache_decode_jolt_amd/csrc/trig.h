@@ -24,6 +24,10 @@
 
 namespace jolt {
 
+// 1 / (2 pi) rounded to float32: radians -> revolutions for the hardware units
+constexpr float kInv2Pi = 0.15915493667125702f;
+
+
 // Domain: |x| < 2^20.  The host enforces it (positions <= 2^20 and
 // 0 <= inv_freq <= 1, true of every RoPE frequency schedule).
 __device__ inline void fast_sincos(float x, float *s, float *c) {
@@ -64,10 +68,10 @@ __device__ inline void rope_angle_cs(int t, float inv_freq, float *c, float *s) 
 // domain), then the hardware sine and cosine units, which take the angle in
 // revolutions.  Same domain as fast_sincos.
 __device__ inline void hw_sincos(float x, float *s, float *c) {
-  const float k = __builtin_rintf(x * 0.15915493667125702f);
+  const float k = __builtin_rintf(x * kInv2Pi);
   float r = __builtin_fmaf(-k, 6.2831854820251465f, x);
   r = __builtin_fmaf(-k, -1.7484555314695172e-07f, r);
-  const float rev = r * 0.15915493667125702f;
+  const float rev = r * kInv2Pi;
   *s = __builtin_amdgcn_sinf(rev);
   *c = __builtin_amdgcn_cosf(rev);
 }

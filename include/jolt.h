@@ -348,8 +348,12 @@ jolt_status jolt_make_rotation(uint64_t seed, int32_t d, double *out);
 /* jolt_debug_sincos: the kernels' float32 sine and cosine of HOST angles[n]
  *   (evaluated on the current device; synchronous), written to HOST outputs.
  *   variant 0: the polynomial evaluation of the float32 paths and of query
- *   RoPE; variant 1: the hardware-unit evaluation of the MFMA key path.
- *   JOLT_E_INVALID for |angle| >= 2^20 or another variant. */
+ *   RoPE; variant 1: the hardware-unit evaluation of the MFMA key path;
+ *   variant 2: the key path's small-angle blocks -- angles[2i] is a position
+ *   t and angles[2i + 1] an inverse frequency f (2n floats in), evaluated as
+ *   the hardware units of t * fl32(f / 2 pi) revolutions.
+ *   JOLT_E_INVALID for |angle| or |t| >= 2^20, f outside [0, 1] or another
+ *   variant. */
 jolt_status jolt_debug_sincos(const float *angles, int32_t n, float *sin_out, float *cos_out,
                               int32_t variant);
 jolt_status jolt_debug_unpack(const jolt_cache *cache, int32_t layer, int32_t tau,

@@ -455,6 +455,26 @@ def test_rope_sincos_accuracy(variant, bound):
     assert worst <= bound, worst
 
 
+def test_rope_small_angle_blocks():
+    """The key path's shortcut for frequency blocks whose angles stay at most
+    128 rad over the launch: position * fl32(inv_freq / 2 pi) straight into the
+    hardware units.  Against sin/cos of the float32 angle fl32(t * inv_freq)
+    (float64) over every (position, frequency) with t * inv_freq <= 128, for
+    both RoPE bases: within 2.5e-5 (three float32 roundings of a value below
+    20.4 revolutions, plus the units' own error)."""
+    worst = 0.0
+    for base in (1e4, 5e5):
+        inv = gen.rope_inv_freq_input(base, 128)
+        t = np.arange(65537, dtype=np.float32)
+        tt, ff = np.meshgrid(t, inv, indexing="ij")
+        keep = tt.astype(np.float64) * ff.astype(np.float64) <= 128.0
+        pairs = np.stack([tt[keep], ff[keep]], axis=1).astype(np.float32)
+        sn, cs = J.jolt_debug_sincos(pairs, 2)
+        a64 = (pairs[:, 0] * pairs[:, 1]).astype(np.float32).astype(np.float64)
+        worst = max(worst, np.max(np.abs(sn - np.sin(a64))), np.max(np.abs(cs - np.cos(a64))))
+    assert worst <= 2.5e-5, worst
+
+
 @pytest.mark.parametrize("split", [512, 1024])
 def test_one_query_two_blocks_per_step(split):
     """One query per KV head on the class with two 16-token blocks per wave
