@@ -25,10 +25,10 @@
 #include <cstdint>
 #include <vector>
 
+#include "errors.h"
 #include "jolt.h"
 
 namespace jolt {
-jolt_status set_error(jolt_status st, const char *fmt, ...);
 }
 
 namespace {
@@ -198,76 +198,78 @@ int64_t grid_size(const Cell &c) {
 
 extern "C" jolt_status jolt_allocate(const jolt_alloc_cell *cells, int32_t n_cells, double budget,
                                      int32_t *choice, double *lambda_out) {
-  if (n_cells < 0 || (n_cells > 0 && (!cells || !choice)) || !(budget >= 0.0))
-    return jolt::set_error(JOLT_E_INVALID, "jolt_allocate: bad arguments");
-  std::vector<Cell> cs(n_cells);
-  for (int i = 0; i < n_cells; ++i) {
-    const jolt_alloc_cell &in = cells[i];
-    if (in.T < 1 || in.d < 1 || in.group_size < 1 || in.n_kv_heads < 1 ||
-        (in.factor_bytes != 2 && in.factor_bytes != 4) || in.n_sT2 < 0 || in.n_sF2 < 0 ||
-        (in.n_sT2 && !in.sT2) || (in.n_sF2 && !in.sF2) || in.cap < 0 || !(in.norm2 >= 0.0))
-      return jolt::set_error(JOLT_E_INVALID, "jolt_allocate: cell %d", i);
-    Cell &c = cs[i];
-    c.T = in.T, c.d = in.d, c.gs = in.group_size, c.H = in.n_kv_heads, c.fb = in.factor_bytes;
-    c.cap = in.cap;
-    c.norm2 = in.norm2;
-    c.cT.assign(1, 0.0);
-    for (int k = 0; k < in.n_sT2; ++k) c.cT.push_back(c.cT.back() + in.sT2[k]);
-    c.cF.assign(1, 0.0);
-    for (int k = 0; k < in.n_sF2; ++k) c.cF.push_back(c.cF.back() + in.sF2[k]);
-    c.phi[0] = 1.0;
-    const double m = m2(c.d);
-    for (int bi = 1; bi < 4; ++bi) {
-      const double L = (double)((1 << kBits[bi]) - 1);
-      c.phi[bi] = m / (3.0 * L * L);
-    }
-  }
-  std::vector<char> exh(n_cells);
-  for (int i = 0; i < n_cells; ++i) exh[i] = grid_size(cs[i]) <= kExhaustiveMax;
-  std::vector<Choice> cur(n_cells);
-  auto choose_all = [&](double lam) {
-    int64_t total = 0;
+  return jolt::guarded("jolt_allocate", [&]() -> jolt_status {
+    if (n_cells < 0 || (n_cells > 0 && (!cells || !choice)) || !(budget >= 0.0))
+      return jolt::set_error(JOLT_E_INVALID, "jolt_allocate: bad arguments");
+    std::vector<Cell> cs(n_cells);
     for (int i = 0; i < n_cells; ++i) {
-      cur[i] = exh[i] ? choose_exhaustive(cs[i], lam) : choose_coordinate(cs[i], lam);
-      total += cs[i].bytes(cur[i].rT, cur[i].rF, kBits[cur[i].bi]);
-    }
-    return total;
-  };
-  double lam = 0.0;
-  if ((double)choose_all(0.0) > budget) {
-    double hi = 1.0;
-    while ((double)choose_all(hi) > budget) {
-      hi *= 2.0;
-      if (hi > 1e300) return jolt::set_error(JOLT_E_INVALID, "jolt_allocate: budget infeasible");
-    }
-    double lo = hi / 2.0;
-    bool done = false;
-    while ((double)choose_all(lo) <= budget) {
-      lo /= 2.0;
-      if (lo < 1e-300) {
-        lam = lo;
-        done = true;
-        break;
+      const jolt_alloc_cell &in = cells[i];
+      if (in.T < 1 || in.d < 1 || in.group_size < 1 || in.n_kv_heads < 1 ||
+          (in.factor_bytes != 2 && in.factor_bytes != 4) || in.n_sT2 < 0 || in.n_sF2 < 0 ||
+          (in.n_sT2 && !in.sT2) || (in.n_sF2 && !in.sF2) || in.cap < 0 || !(in.norm2 >= 0.0))
+        return jolt::set_error(JOLT_E_INVALID, "jolt_allocate: cell %d", i);
+      Cell &c = cs[i];
+      c.T = in.T, c.d = in.d, c.gs = in.group_size, c.H = in.n_kv_heads, c.fb = in.factor_bytes;
+      c.cap = in.cap;
+      c.norm2 = in.norm2;
+      c.cT.assign(1, 0.0);
+      for (int k = 0; k < in.n_sT2; ++k) c.cT.push_back(c.cT.back() + in.sT2[k]);
+      c.cF.assign(1, 0.0);
+      for (int k = 0; k < in.n_sF2; ++k) c.cF.push_back(c.cF.back() + in.sF2[k]);
+      c.phi[0] = 1.0;
+      const double m = m2(c.d);
+      for (int bi = 1; bi < 4; ++bi) {
+        const double L = (double)((1 << kBits[bi]) - 1);
+        c.phi[bi] = m / (3.0 * L * L);
       }
     }
-    if (!done) {
-      for (int it = 0; it < 200; ++it) {
-        const double mid = std::sqrt(lo * hi);
-        if (!(lo < mid && mid < hi)) break;
-        if ((double)choose_all(mid) <= budget)
-          hi = mid;
-        else
-          lo = mid;
+    std::vector<char> exh(n_cells);
+    for (int i = 0; i < n_cells; ++i) exh[i] = grid_size(cs[i]) <= kExhaustiveMax;
+    std::vector<Choice> cur(n_cells);
+    auto choose_all = [&](double lam) {
+      int64_t total = 0;
+      for (int i = 0; i < n_cells; ++i) {
+        cur[i] = exh[i] ? choose_exhaustive(cs[i], lam) : choose_coordinate(cs[i], lam);
+        total += cs[i].bytes(cur[i].rT, cur[i].rF, kBits[cur[i].bi]);
       }
-      lam = hi;
+      return total;
+    };
+    double lam = 0.0;
+    if ((double)choose_all(0.0) > budget) {
+      double hi = 1.0;
+      while ((double)choose_all(hi) > budget) {
+        hi *= 2.0;
+        if (hi > 1e300) return jolt::set_error(JOLT_E_INVALID, "jolt_allocate: budget infeasible");
+      }
+      double lo = hi / 2.0;
+      bool done = false;
+      while ((double)choose_all(lo) <= budget) {
+        lo /= 2.0;
+        if (lo < 1e-300) {
+          lam = lo;
+          done = true;
+          break;
+        }
+      }
+      if (!done) {
+        for (int it = 0; it < 200; ++it) {
+          const double mid = std::sqrt(lo * hi);
+          if (!(lo < mid && mid < hi)) break;
+          if ((double)choose_all(mid) <= budget)
+            hi = mid;
+          else
+            lo = mid;
+        }
+        lam = hi;
+      }
+      choose_all(lam);
     }
-    choose_all(lam);
-  }
-  for (int i = 0; i < n_cells; ++i) {
-    choice[3 * i] = cur[i].rT;
-    choice[3 * i + 1] = cur[i].rF;
-    choice[3 * i + 2] = kBits[cur[i].bi];
-  }
-  if (lambda_out) *lambda_out = lam;
-  return jolt::set_error(JOLT_OK, "");
+    for (int i = 0; i < n_cells; ++i) {
+      choice[3 * i] = cur[i].rT;
+      choice[3 * i + 1] = cur[i].rF;
+      choice[3 * i + 2] = kBits[cur[i].bi];
+    }
+    if (lambda_out) *lambda_out = lam;
+    return jolt::set_error(JOLT_OK, "");
+  });
 }

@@ -27,12 +27,10 @@
 #include <vector>
 
 #include "compress.h"
+#include "errors.h"
 #include "jolt.h"
 #include "layout.h"
 
-namespace jolt {
-jolt_status set_error(jolt_status st, const char *fmt, ...);
-}
 using namespace jolt;
 
 namespace {
@@ -294,32 +292,34 @@ extern "C" jolt_status jolt_flash_spectra(const void *X, jolt_dtype x_dtype, int
                                           int32_t n_kv_heads, int32_t T, int32_t head_dim,
                                           const jolt_flash_params *p, double *sT2, double *sF2,
                                           double *norm2, jolt_stream stream) {
-  std::string why;
-  if (!check_shape(X, x_dtype, group_size, n_kv_heads, T, head_dim, p, &why))
-    return set_error(JOLT_E_INVALID, "jolt_flash_spectra: %s", why.c_str());
-  if (!sT2 || !sF2 || !norm2) return set_error(JOLT_E_INVALID, "NULL output");
-  Ctx cx;
-  cx.s = (hipStream_t)stream;
-  if (rocblas_create_handle(&cx.h) != rocblas_status_success)
-    return set_error(JOLT_E_HIP, "rocblas_create_handle failed");
-  rocblas_set_stream(cx.h, cx.s);
-  const Shape sh{group_size, n_kv_heads, T, head_dim, x_dtype == JOLT_F32 ? 1 : 2};
-  DevMem U;
-  int q = 0;
-  std::vector<double> sig, ev;
-  double n2 = 0.0;
-  if (!token_basis(cx, sh, X, *p, U, &q, sig) || !feature_gram(cx, sh, X, ev, &n2))
-    return set_error(JOLT_E_HIP, "jolt_flash_spectra: %s", cx.err.c_str());
-  double acc = 0.0;
-  for (int i = 0; i < p->q_cap; ++i) {
-    const double v = i < q ? sig[i] * sig[i] : 0.0;
-    sT2[i] = v;
-    acc += v;
-  }
-  sT2[p->q_cap] = std::max(n2 - acc, 0.0);
-  for (int i = 0; i < head_dim; ++i) sF2[i] = ev[i];
-  *norm2 = n2;
-  return set_error(JOLT_OK, "");
+  return jolt::guarded("jolt_flash_spectra", [&]() -> jolt_status {
+    std::string why;
+    if (!check_shape(X, x_dtype, group_size, n_kv_heads, T, head_dim, p, &why))
+      return set_error(JOLT_E_INVALID, "jolt_flash_spectra: %s", why.c_str());
+    if (!sT2 || !sF2 || !norm2) return set_error(JOLT_E_INVALID, "NULL output");
+    Ctx cx;
+    cx.s = (hipStream_t)stream;
+    if (rocblas_create_handle(&cx.h) != rocblas_status_success)
+      return set_error(JOLT_E_HIP, "rocblas_create_handle failed");
+    rocblas_set_stream(cx.h, cx.s);
+    const Shape sh{group_size, n_kv_heads, T, head_dim, x_dtype == JOLT_F32 ? 1 : 2};
+    DevMem U;
+    int q = 0;
+    std::vector<double> sig, ev;
+    double n2 = 0.0;
+    if (!token_basis(cx, sh, X, *p, U, &q, sig) || !feature_gram(cx, sh, X, ev, &n2))
+      return set_error(JOLT_E_HIP, "jolt_flash_spectra: %s", cx.err.c_str());
+    double acc = 0.0;
+    for (int i = 0; i < p->q_cap; ++i) {
+      const double v = i < q ? sig[i] * sig[i] : 0.0;
+      sT2[i] = v;
+      acc += v;
+    }
+    sT2[p->q_cap] = std::max(n2 - acc, 0.0);
+    for (int i = 0; i < head_dim; ++i) sF2[i] = ev[i];
+    *norm2 = n2;
+    return set_error(JOLT_OK, "");
+  });
 }
 
 extern "C" jolt_status jolt_flash_compress_cell(
@@ -327,137 +327,139 @@ extern "C" jolt_status jolt_flash_compress_cell(
     int32_t head_dim, const jolt_flash_params *p, int32_t r_T, int32_t r_F, int32_t bits,
     uint64_t rotation_seed, jolt_dtype factor_dtype, void *A, void *B, void *G, uint8_t *codes,
     float *scales, jolt_stream stream) {
-  std::string why;
-  if (!check_shape(X, x_dtype, group_size, n_kv_heads, T, head_dim, p, &why))
-    return set_error(JOLT_E_INVALID, "jolt_flash_compress_cell: %s", why.c_str());
-  const int d = head_dim;
-  if (r_T < 0 || r_F < 0 || r_F > d || (r_T == 0) != (r_F == 0) ||
-      r_T > std::min<int64_t>(T, (int64_t)group_size * n_kv_heads * d))
-    return set_error(JOLT_E_INVALID, "ranks r_T=%d r_F=%d", r_T, r_F);
-  if (r_T > p->q_cap) return set_error(JOLT_E_INVALID, "r_T=%d above q_cap=%d", r_T, p->q_cap);
-  if (bits != 0 && bits != 2 && bits != 4 && bits != 8)
-    return set_error(JOLT_E_INVALID, "bits=%d", bits);
-  if (factor_dtype != JOLT_F32 && factor_dtype != JOLT_BF16)
-    return set_error(JOLT_E_INVALID, "factor dtype");
-  if (r_T > 0 && (!A || !B || !G)) return set_error(JOLT_E_INVALID, "NULL factor output");
-  if (bits > 0 && (!codes || !scales)) return set_error(JOLT_E_INVALID, "NULL code output");
-  if (bits > 0 && (d * bits) % 8) return set_error(JOLT_E_INVALID, "d * bits not a byte multiple");
+  return jolt::guarded("jolt_flash_compress_cell", [&]() -> jolt_status {
+    std::string why;
+    if (!check_shape(X, x_dtype, group_size, n_kv_heads, T, head_dim, p, &why))
+      return set_error(JOLT_E_INVALID, "jolt_flash_compress_cell: %s", why.c_str());
+    const int d = head_dim;
+    if (r_T < 0 || r_F < 0 || r_F > d || (r_T == 0) != (r_F == 0) ||
+        r_T > std::min<int64_t>(T, (int64_t)group_size * n_kv_heads * d))
+      return set_error(JOLT_E_INVALID, "ranks r_T=%d r_F=%d", r_T, r_F);
+    if (r_T > p->q_cap) return set_error(JOLT_E_INVALID, "r_T=%d above q_cap=%d", r_T, p->q_cap);
+    if (bits != 0 && bits != 2 && bits != 4 && bits != 8)
+      return set_error(JOLT_E_INVALID, "bits=%d", bits);
+    if (factor_dtype != JOLT_F32 && factor_dtype != JOLT_BF16)
+      return set_error(JOLT_E_INVALID, "factor dtype");
+    if (r_T > 0 && (!A || !B || !G)) return set_error(JOLT_E_INVALID, "NULL factor output");
+    if (bits > 0 && (!codes || !scales)) return set_error(JOLT_E_INVALID, "NULL code output");
+    if (bits > 0 && (d * bits) % 8) return set_error(JOLT_E_INVALID, "d * bits not a byte multiple");
 
-  Ctx cx;
-  cx.s = (hipStream_t)stream;
-  if (rocblas_create_handle(&cx.h) != rocblas_status_success)
-    return set_error(JOLT_E_HIP, "rocblas_create_handle failed");
-  rocblas_set_stream(cx.h, cx.s);
-  const Shape sh{group_size, n_kv_heads, T, d, x_dtype == JOLT_F32 ? 1 : 2};
-  const int64_t nb = sh.nb();
-  const int fbytes = factor_dtype == JOLT_BF16 ? 2 : 4;
-  const int bf = factor_dtype == JOLT_BF16 ? 1 : 0;
-  auto run = [&]() -> bool {
-    DevMem dA, dB, dG, dSa, dSb, dSg, dW, dInfo;
-    if (!dalloc(cx, dInfo, sizeof(int))) return false;
-    if (r_T > 0) {
-      DevMem U, dYp, dF;
-      int q = 0;
-      std::vector<double> sig;
-      if (!token_basis(cx, sh, X, *p, U, &q, sig)) return false;
-      // A = U[:, :r_T]
-      if (!dalloc(cx, dA, sizeof(double) * T * r_T)) return false;
-      CK(hipMemcpy2DAsync(dA.p, sizeof(double) * r_T, U.p, sizeof(double) * q, sizeof(double) * r_T,
-                          T, hipMemcpyDeviceToDevice, cx.s));
-      // Y[l, h] = A^T X[l, h]  (r_T x d)
-      if (!dalloc(cx, dYp, sizeof(double) * nb * r_T * d)) return false;
-      GemmOp g;
-      g.A = dA.p, g.a_i = 1, g.a_k = r_T, g.a_b = 0;
-      g.B = X, g.b_k = d, g.b_j = 1, g.b_b = (int64_t)T * d;
-      g.C = dYp.get<double>(), g.c_i = d, g.c_j = 1, g.c_b = (int64_t)r_T * d;
-      g.M = r_T, g.N = d, g.K = T, g.batch = (int)nb;
-      if (!gemm(cx, g, 0, sh.tx, 0)) return false;
-      // feature basis: leading r_F eigenvectors of sum_lh Y^T Y
-      if (!dalloc(cx, dF, sizeof(double) * d * d)) return false;
-      g = GemmOp();
-      g.A = dYp.p, g.a_i = 1, g.a_k = d, g.a_b = (int64_t)r_T * d;
-      g.B = dYp.p, g.b_k = d, g.b_j = 1, g.b_b = (int64_t)r_T * d;
-      g.C = dF.get<double>(), g.c_i = d, g.c_j = 1;
-      g.M = d, g.N = d, g.K = r_T, g.batch = (int)nb, g.sum_batch = 1;
-      if (!gemm(cx, g)) return false;
-      std::vector<double> w;
-      if (!eigh(cx, dF.get<double>(), d, w, dInfo.get<int>())) return false;
-      std::vector<double> V((size_t)d * d), hB((size_t)d * r_F);
-      CK(hipMemcpyAsync(V.data(), dF.p, sizeof(double) * d * d, hipMemcpyDeviceToHost, cx.s));
-      CK(hipStreamSynchronize(cx.s));
-      for (int f = 0; f < d; ++f)
-        for (int c = 0; c < r_F; ++c) hB[(size_t)f * r_F + c] = V[(size_t)f + (size_t)(d - 1 - c) * d];
-      if (!dalloc(cx, dB, sizeof(double) * d * r_F)) return false;
-      CK(hipMemcpyAsync(dB.p, hB.data(), sizeof(double) * hB.size(), hipMemcpyHostToDevice, cx.s));
-      // G[l, h] = Y[l, h] B  (r_T x r_F)
-      if (!dalloc(cx, dG, sizeof(double) * nb * r_T * r_F)) return false;
-      g = GemmOp();
-      g.A = dYp.p, g.a_i = d, g.a_k = 1, g.a_b = (int64_t)r_T * d;
-      g.B = dB.p, g.b_k = r_F, g.b_j = 1, g.b_b = 0;
-      g.C = dG.get<double>(), g.c_i = r_F, g.c_j = 1, g.c_b = (int64_t)r_T * r_F;
-      g.M = r_T, g.N = r_F, g.K = d, g.batch = (int)nb;
-      if (!gemm(cx, g)) return false;
-      // round to the storage dtype (in place) and keep the stored bits
-      const int64_t nA = (int64_t)T * r_T, nB = (int64_t)d * r_F, nG = nb * r_T * r_F;
-      if (!dalloc(cx, dSa, fbytes * nA) || !dalloc(cx, dSb, fbytes * nB) || !dalloc(cx, dSg, fbytes * nG))
-        return false;
-      CK(round_store_launch(dA.get<double>(), nA, bf, dSa.p, cx.s));
-      CK(round_store_launch(dB.get<double>(), nB, bf, dSb.p, cx.s));
-      CK(round_store_launch(dG.get<double>(), nG, bf, dSg.p, cx.s));
-      CK(hipMemcpyAsync(A, dSa.p, fbytes * nA, hipMemcpyDeviceToHost, cx.s));
-      CK(hipMemcpyAsync(B, dSb.p, fbytes * nB, hipMemcpyDeviceToHost, cx.s));
-      CK(hipMemcpyAsync(G, dSg.p, fbytes * nG, hipMemcpyDeviceToHost, cx.s));
+    Ctx cx;
+    cx.s = (hipStream_t)stream;
+    if (rocblas_create_handle(&cx.h) != rocblas_status_success)
+      return set_error(JOLT_E_HIP, "rocblas_create_handle failed");
+    rocblas_set_stream(cx.h, cx.s);
+    const Shape sh{group_size, n_kv_heads, T, d, x_dtype == JOLT_F32 ? 1 : 2};
+    const int64_t nb = sh.nb();
+    const int fbytes = factor_dtype == JOLT_BF16 ? 2 : 4;
+    const int bf = factor_dtype == JOLT_BF16 ? 1 : 0;
+    auto run = [&]() -> bool {
+      DevMem dA, dB, dG, dSa, dSb, dSg, dW, dInfo;
+      if (!dalloc(cx, dInfo, sizeof(int))) return false;
+      if (r_T > 0) {
+        DevMem U, dYp, dF;
+        int q = 0;
+        std::vector<double> sig;
+        if (!token_basis(cx, sh, X, *p, U, &q, sig)) return false;
+        // A = U[:, :r_T]
+        if (!dalloc(cx, dA, sizeof(double) * T * r_T)) return false;
+        CK(hipMemcpy2DAsync(dA.p, sizeof(double) * r_T, U.p, sizeof(double) * q, sizeof(double) * r_T,
+                            T, hipMemcpyDeviceToDevice, cx.s));
+        // Y[l, h] = A^T X[l, h]  (r_T x d)
+        if (!dalloc(cx, dYp, sizeof(double) * nb * r_T * d)) return false;
+        GemmOp g;
+        g.A = dA.p, g.a_i = 1, g.a_k = r_T, g.a_b = 0;
+        g.B = X, g.b_k = d, g.b_j = 1, g.b_b = (int64_t)T * d;
+        g.C = dYp.get<double>(), g.c_i = d, g.c_j = 1, g.c_b = (int64_t)r_T * d;
+        g.M = r_T, g.N = d, g.K = T, g.batch = (int)nb;
+        if (!gemm(cx, g, 0, sh.tx, 0)) return false;
+        // feature basis: leading r_F eigenvectors of sum_lh Y^T Y
+        if (!dalloc(cx, dF, sizeof(double) * d * d)) return false;
+        g = GemmOp();
+        g.A = dYp.p, g.a_i = 1, g.a_k = d, g.a_b = (int64_t)r_T * d;
+        g.B = dYp.p, g.b_k = d, g.b_j = 1, g.b_b = (int64_t)r_T * d;
+        g.C = dF.get<double>(), g.c_i = d, g.c_j = 1;
+        g.M = d, g.N = d, g.K = r_T, g.batch = (int)nb, g.sum_batch = 1;
+        if (!gemm(cx, g)) return false;
+        std::vector<double> w;
+        if (!eigh(cx, dF.get<double>(), d, w, dInfo.get<int>())) return false;
+        std::vector<double> V((size_t)d * d), hB((size_t)d * r_F);
+        CK(hipMemcpyAsync(V.data(), dF.p, sizeof(double) * d * d, hipMemcpyDeviceToHost, cx.s));
+        CK(hipStreamSynchronize(cx.s));
+        for (int f = 0; f < d; ++f)
+          for (int c = 0; c < r_F; ++c) hB[(size_t)f * r_F + c] = V[(size_t)f + (size_t)(d - 1 - c) * d];
+        if (!dalloc(cx, dB, sizeof(double) * d * r_F)) return false;
+        CK(hipMemcpyAsync(dB.p, hB.data(), sizeof(double) * hB.size(), hipMemcpyHostToDevice, cx.s));
+        // G[l, h] = Y[l, h] B  (r_T x r_F)
+        if (!dalloc(cx, dG, sizeof(double) * nb * r_T * r_F)) return false;
+        g = GemmOp();
+        g.A = dYp.p, g.a_i = d, g.a_k = 1, g.a_b = (int64_t)r_T * d;
+        g.B = dB.p, g.b_k = r_F, g.b_j = 1, g.b_b = 0;
+        g.C = dG.get<double>(), g.c_i = r_F, g.c_j = 1, g.c_b = (int64_t)r_T * r_F;
+        g.M = r_T, g.N = r_F, g.K = d, g.batch = (int)nb;
+        if (!gemm(cx, g)) return false;
+        // round to the storage dtype (in place) and keep the stored bits
+        const int64_t nA = (int64_t)T * r_T, nB = (int64_t)d * r_F, nG = nb * r_T * r_F;
+        if (!dalloc(cx, dSa, fbytes * nA) || !dalloc(cx, dSb, fbytes * nB) || !dalloc(cx, dSg, fbytes * nG))
+          return false;
+        CK(round_store_launch(dA.get<double>(), nA, bf, dSa.p, cx.s));
+        CK(round_store_launch(dB.get<double>(), nB, bf, dSb.p, cx.s));
+        CK(round_store_launch(dG.get<double>(), nG, bf, dSg.p, cx.s));
+        CK(hipMemcpyAsync(A, dSa.p, fbytes * nA, hipMemcpyDeviceToHost, cx.s));
+        CK(hipMemcpyAsync(B, dSb.p, fbytes * nB, hipMemcpyDeviceToHost, cx.s));
+        CK(hipMemcpyAsync(G, dSg.p, fbytes * nG, hipMemcpyDeviceToHost, cx.s));
+        if (bits > 0) {
+          // W[l, h] = G_s[l, h] B_s^T  (r_T x d)
+          if (!dalloc(cx, dW, sizeof(double) * nb * r_T * d)) return false;
+          g = GemmOp();
+          g.A = dG.p, g.a_i = r_F, g.a_k = 1, g.a_b = (int64_t)r_T * r_F;
+          g.B = dB.p, g.b_k = 1, g.b_j = r_F, g.b_b = 0;
+          g.C = dW.get<double>(), g.c_i = d, g.c_j = 1, g.c_b = (int64_t)r_T * d;
+          g.M = r_T, g.N = d, g.K = r_F, g.batch = (int)nb;
+          if (!gemm(cx, g)) return false;
+        }
+      }
       if (bits > 0) {
-        // W[l, h] = G_s[l, h] B_s^T  (r_T x d)
-        if (!dalloc(cx, dW, sizeof(double) * nb * r_T * d)) return false;
-        g = GemmOp();
-        g.A = dG.p, g.a_i = r_F, g.a_k = 1, g.a_b = (int64_t)r_T * r_F;
-        g.B = dB.p, g.b_k = 1, g.b_j = r_F, g.b_b = 0;
-        g.C = dW.get<double>(), g.c_i = d, g.c_j = 1, g.c_b = (int64_t)r_T * d;
-        g.M = r_T, g.N = d, g.K = r_F, g.batch = (int)nb;
-        if (!gemm(cx, g)) return false;
+        // R[l, h] = X[l, h] - A_s W[l, h], then R' = R Pi, then codes
+        const int64_t rows = nb * T;
+        DevMem dR, dRp, dPi, dCodes, dScales;
+        if (!dalloc(cx, dR, sizeof(double) * rows * d) || !dalloc(cx, dRp, sizeof(double) * rows * d) ||
+            !dalloc(cx, dPi, sizeof(double) * d * d) || !dalloc(cx, dCodes, rows * d * bits / 8) ||
+            !dalloc(cx, dScales, sizeof(float) * rows))
+          return false;
+        GemmOp g;
+        g.A = r_T > 0 ? dA.p : nullptr, g.a_i = r_T, g.a_k = 1, g.a_b = 0;
+        g.B = r_T > 0 ? dW.p : nullptr, g.b_k = d, g.b_j = 1, g.b_b = (int64_t)r_T * d;
+        g.D = X, g.d_i = d, g.d_j = 1, g.d_b = (int64_t)T * d;
+        g.C = dR.get<double>(), g.c_i = d, g.c_j = 1, g.c_b = (int64_t)T * d;
+        g.M = T, g.N = d, g.K = r_T, g.batch = (int)nb;
+        g.alpha = -1.0, g.beta = 1.0;
+        if (!gemm(cx, g, 0, 0, sh.tx)) return false;
+        std::vector<double> Pi((size_t)d * d);
+        make_rotation(rotation_seed, d, Pi.data());
+        CK(hipMemcpyAsync(dPi.p, Pi.data(), sizeof(double) * d * d, hipMemcpyHostToDevice, cx.s));
+        // R' = R Pi over all rows, in chunks the grid can hold
+        const int64_t chunk = (int64_t)60000 * 64;
+        for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
+          g = GemmOp();
+          g.A = dR.get<double>() + r0 * d, g.a_i = d, g.a_k = 1;
+          g.B = dPi.p, g.b_k = d, g.b_j = 1;
+          g.C = dRp.get<double>() + r0 * d, g.c_i = d, g.c_j = 1;
+          g.M = (int)std::min(chunk, rows - r0), g.N = d, g.K = d;
+          if (!gemm(cx, g)) return false;
+        }
+        CK(quantize_rows_launch(dRp.get<double>(), rows, d, bits, dCodes.get<uint8_t>(),
+                                dScales.get<float>(), cx.s));
+        CK(hipMemcpyAsync(codes, dCodes.p, rows * d * bits / 8, hipMemcpyDeviceToHost, cx.s));
+        CK(hipMemcpyAsync(scales, dScales.p, sizeof(float) * rows, hipMemcpyDeviceToHost, cx.s));
+        CK(hipStreamSynchronize(cx.s));
       }
-    }
-    if (bits > 0) {
-      // R[l, h] = X[l, h] - A_s W[l, h], then R' = R Pi, then codes
-      const int64_t rows = nb * T;
-      DevMem dR, dRp, dPi, dCodes, dScales;
-      if (!dalloc(cx, dR, sizeof(double) * rows * d) || !dalloc(cx, dRp, sizeof(double) * rows * d) ||
-          !dalloc(cx, dPi, sizeof(double) * d * d) || !dalloc(cx, dCodes, rows * d * bits / 8) ||
-          !dalloc(cx, dScales, sizeof(float) * rows))
-        return false;
-      GemmOp g;
-      g.A = r_T > 0 ? dA.p : nullptr, g.a_i = r_T, g.a_k = 1, g.a_b = 0;
-      g.B = r_T > 0 ? dW.p : nullptr, g.b_k = d, g.b_j = 1, g.b_b = (int64_t)r_T * d;
-      g.D = X, g.d_i = d, g.d_j = 1, g.d_b = (int64_t)T * d;
-      g.C = dR.get<double>(), g.c_i = d, g.c_j = 1, g.c_b = (int64_t)T * d;
-      g.M = T, g.N = d, g.K = r_T, g.batch = (int)nb;
-      g.alpha = -1.0, g.beta = 1.0;
-      if (!gemm(cx, g, 0, 0, sh.tx)) return false;
-      std::vector<double> Pi((size_t)d * d);
-      make_rotation(rotation_seed, d, Pi.data());
-      CK(hipMemcpyAsync(dPi.p, Pi.data(), sizeof(double) * d * d, hipMemcpyHostToDevice, cx.s));
-      // R' = R Pi over all rows, in chunks the grid can hold
-      const int64_t chunk = (int64_t)60000 * 64;
-      for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
-        g = GemmOp();
-        g.A = dR.get<double>() + r0 * d, g.a_i = d, g.a_k = 1;
-        g.B = dPi.p, g.b_k = d, g.b_j = 1;
-        g.C = dRp.get<double>() + r0 * d, g.c_i = d, g.c_j = 1;
-        g.M = (int)std::min(chunk, rows - r0), g.N = d, g.K = d;
-        if (!gemm(cx, g)) return false;
-      }
-      CK(quantize_rows_launch(dRp.get<double>(), rows, d, bits, dCodes.get<uint8_t>(),
-                              dScales.get<float>(), cx.s));
-      CK(hipMemcpyAsync(codes, dCodes.p, rows * d * bits / 8, hipMemcpyDeviceToHost, cx.s));
-      CK(hipMemcpyAsync(scales, dScales.p, sizeof(float) * rows, hipMemcpyDeviceToHost, cx.s));
       CK(hipStreamSynchronize(cx.s));
-    }
-    CK(hipStreamSynchronize(cx.s));
-    return true;
-  };
-  if (!run()) return set_error(JOLT_E_HIP, "jolt_flash_compress_cell: %s", cx.err.c_str());
-  return set_error(JOLT_OK, "");
+      return true;
+    };
+    if (!run()) return set_error(JOLT_E_HIP, "jolt_flash_compress_cell: %s", cx.err.c_str());
+    return set_error(JOLT_OK, "");
+  });
 }
 
 // Alignment-based layer grouping ("A JoLT for the KV cache" §3): each
@@ -472,66 +474,68 @@ extern "C" jolt_status jolt_flash_layer_groups(const void *const *k_layers,
                                                double tau, int32_t max_group,
                                                int32_t *group_start, int32_t *n_groups,
                                                double *align, jolt_stream stream) {
-  std::string why;
-  if (!k_layers || !v_layers || !group_start || !n_groups || n_layers < 1 || max_group < 0)
-    return set_error(JOLT_E_INVALID, "jolt_flash_layer_groups: bad arguments");
-  for (int l = 0; l < n_layers; ++l)
-    if (!check_shape(k_layers[l], x_dtype, 2, n_kv_heads, T, head_dim, p, &why) || !v_layers[l])
-      return set_error(JOLT_E_INVALID, "jolt_flash_layer_groups: layer %d: %s", l,
-                       why.empty() ? "NULL values" : why.c_str());
-  Ctx cx;
-  cx.s = (hipStream_t)stream;
-  if (rocblas_create_handle(&cx.h) != rocblas_status_success)
-    return set_error(JOLT_E_HIP, "rocblas_create_handle failed");
-  rocblas_set_stream(cx.h, cx.s);
-  const int eb = x_dtype == JOLT_F32 ? 4 : 2;
-  const size_t half = (size_t)n_kv_heads * T * head_dim * eb;
-  const Shape sh{2, n_kv_heads, T, head_dim, x_dtype == JOLT_F32 ? 1 : 2};
-  std::vector<double> a(n_layers > 1 ? n_layers - 1 : 0);
-  auto run = [&]() -> bool {
-    DevMem dX, dC, prevU;
-    int prev_q = 0;
-    if (!dalloc(cx, dX, 2 * half)) return false;
-    for (int l = 0; l < n_layers; ++l) {
-      // keys then values of the layer, contiguous: [2][H][T][d]
-      CK(hipMemcpyAsync(dX.p, k_layers[l], half, hipMemcpyDeviceToDevice, cx.s));
-      CK(hipMemcpyAsync((uint8_t *)dX.p + half, v_layers[l], half, hipMemcpyDeviceToDevice, cx.s));
-      DevMem U;
-      int q = 0;
-      std::vector<double> sig;
-      if (!token_basis(cx, sh, dX.p, *p, U, &q, sig)) return false;
-      if (l > 0) {
-        if (!dC.p && !dalloc(cx, dC, sizeof(double) * q * q)) return false;
-        GemmOp g;
-        g.A = prevU.p, g.a_i = 1, g.a_k = prev_q;
-        g.B = U.p, g.b_k = q, g.b_j = 1;
-        g.C = dC.get<double>(), g.c_i = q, g.c_j = 1;
-        g.M = prev_q, g.N = q, g.K = T;
-        if (!gemm(cx, g)) return false;
-        std::vector<double> hc((size_t)prev_q * q);
-        CK(hipMemcpyAsync(hc.data(), dC.p, sizeof(double) * hc.size(), hipMemcpyDeviceToHost, cx.s));
-        CK(hipStreamSynchronize(cx.s));
-        double ss = 0.0;
-        for (double v : hc) ss += v * v;
-        a[l - 1] = ss / prev_q;
+  return jolt::guarded("jolt_flash_layer_groups", [&]() -> jolt_status {
+    std::string why;
+    if (!k_layers || !v_layers || !group_start || !n_groups || n_layers < 1 || max_group < 0)
+      return set_error(JOLT_E_INVALID, "jolt_flash_layer_groups: bad arguments");
+    for (int l = 0; l < n_layers; ++l)
+      if (!check_shape(k_layers[l], x_dtype, 2, n_kv_heads, T, head_dim, p, &why) || !v_layers[l])
+        return set_error(JOLT_E_INVALID, "jolt_flash_layer_groups: layer %d: %s", l,
+                         why.empty() ? "NULL values" : why.c_str());
+    Ctx cx;
+    cx.s = (hipStream_t)stream;
+    if (rocblas_create_handle(&cx.h) != rocblas_status_success)
+      return set_error(JOLT_E_HIP, "rocblas_create_handle failed");
+    rocblas_set_stream(cx.h, cx.s);
+    const int eb = x_dtype == JOLT_F32 ? 4 : 2;
+    const size_t half = (size_t)n_kv_heads * T * head_dim * eb;
+    const Shape sh{2, n_kv_heads, T, head_dim, x_dtype == JOLT_F32 ? 1 : 2};
+    std::vector<double> a(n_layers > 1 ? n_layers - 1 : 0);
+    auto run = [&]() -> bool {
+      DevMem dX, dC, prevU;
+      int prev_q = 0;
+      if (!dalloc(cx, dX, 2 * half)) return false;
+      for (int l = 0; l < n_layers; ++l) {
+        // keys then values of the layer, contiguous: [2][H][T][d]
+        CK(hipMemcpyAsync(dX.p, k_layers[l], half, hipMemcpyDeviceToDevice, cx.s));
+        CK(hipMemcpyAsync((uint8_t *)dX.p + half, v_layers[l], half, hipMemcpyDeviceToDevice, cx.s));
+        DevMem U;
+        int q = 0;
+        std::vector<double> sig;
+        if (!token_basis(cx, sh, dX.p, *p, U, &q, sig)) return false;
+        if (l > 0) {
+          if (!dC.p && !dalloc(cx, dC, sizeof(double) * q * q)) return false;
+          GemmOp g;
+          g.A = prevU.p, g.a_i = 1, g.a_k = prev_q;
+          g.B = U.p, g.b_k = q, g.b_j = 1;
+          g.C = dC.get<double>(), g.c_i = q, g.c_j = 1;
+          g.M = prev_q, g.N = q, g.K = T;
+          if (!gemm(cx, g)) return false;
+          std::vector<double> hc((size_t)prev_q * q);
+          CK(hipMemcpyAsync(hc.data(), dC.p, sizeof(double) * hc.size(), hipMemcpyDeviceToHost, cx.s));
+          CK(hipStreamSynchronize(cx.s));
+          double ss = 0.0;
+          for (double v : hc) ss += v * v;
+          a[l - 1] = ss / prev_q;
+        }
+        std::swap(prevU.p, U.p);
+        prev_q = q;
       }
-      std::swap(prevU.p, U.p);
-      prev_q = q;
+      return true;
+    };
+    if (!run()) return set_error(JOLT_E_HIP, "jolt_flash_layer_groups: %s", cx.err.c_str());
+    int ng = 0;
+    group_start[0] = 0;
+    for (int l = 1; l < n_layers; ++l) {
+      const int size = l - group_start[ng];
+      if (a[l - 1] < tau || (max_group > 0 && size >= max_group)) group_start[++ng] = l;
     }
-    return true;
-  };
-  if (!run()) return set_error(JOLT_E_HIP, "jolt_flash_layer_groups: %s", cx.err.c_str());
-  int ng = 0;
-  group_start[0] = 0;
-  for (int l = 1; l < n_layers; ++l) {
-    const int size = l - group_start[ng];
-    if (a[l - 1] < tau || (max_group > 0 && size >= max_group)) group_start[++ng] = l;
-  }
-  group_start[++ng] = n_layers;
-  *n_groups = ng;
-  if (align)
-    for (int l = 0; l + 1 < n_layers; ++l) align[l] = a[l];
-  return set_error(JOLT_OK, "");
+    group_start[++ng] = n_layers;
+    *n_groups = ng;
+    if (align)
+      for (int l = 0; l + 1 < n_layers; ++l) align[l] = a[l];
+    return set_error(JOLT_OK, "");
+  });
 }
 
 extern "C" jolt_status jolt_quantize_rows(const double *rows, int64_t n_rows, int32_t d, int32_t bits,

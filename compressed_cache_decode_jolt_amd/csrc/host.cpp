@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "jolt.h"
+#include "errors.h"
 #include "jolt_internal.h"
 
 using namespace jolt;
@@ -223,6 +224,10 @@ extern "C" jolt_status jolt_load_cache(const jolt_cache_desc *desc, jolt_stream 
     if (c->dev) (void)hipFree(c->dev);
     delete c;
     return fail(JOLT_E_OOM, "host staging allocation failed");
+  } catch (const std::exception &e) {
+    if (c->dev) (void)hipFree(c->dev);
+    delete c;
+    return fail(JOLT_E_INVALID, "host staging: %s", e.what());
   }
   *out = c;
   return ok();
@@ -805,9 +810,11 @@ extern "C" jolt_status jolt_dense_attention(const void *k_rope, const void *v, j
 
 // --------------------------------------------------------- test helpers --
 extern "C" jolt_status jolt_make_rotation(uint64_t seed, int32_t d, double *out) {
-  if (!out || d < 1 || d > 4096) return fail(JOLT_E_INVALID, "out NULL or d=%d", d);
-  jolt::make_rotation(seed, d, out);
-  return ok();
+  return jolt::guarded("jolt_make_rotation", [&]() -> jolt_status {
+    if (!out || d < 1 || d > 4096) return fail(JOLT_E_INVALID, "out NULL or d=%d", d);
+    jolt::make_rotation(seed, d, out);
+    return ok();
+  });
 }
 
 extern "C" jolt_status jolt_debug_unpack(const jolt_cache *c, int32_t layer, int32_t tau,

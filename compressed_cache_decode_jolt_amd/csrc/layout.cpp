@@ -6,6 +6,8 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <exception>
+#include <mutex>
 #include <thread>
 
 namespace jolt {
@@ -44,18 +46,31 @@ template <class F>
 static void parallel_for(int n, int threads, F f) {
   int nt = threads > 0 ? threads : (int)std::max(1u, std::thread::hardware_concurrency());
   nt = std::min(nt, n);
-  if (nt <= 1) {
-    for (int i = 0; i < n; ++i) f(i);
-    return;
-  }
   std::atomic<int> next{0};
-  std::vector<std::thread> pool;
-  pool.reserve(nt);
-  for (int t = 0; t < nt; ++t)
-    pool.emplace_back([&] {
+  std::exception_ptr err;
+  std::mutex mu;
+  // an exception in a work item stops the others and is rethrown below, on
+  // the calling thread
+  auto work = [&] {
+    try {
       for (int i; (i = next.fetch_add(1)) < n;) f(i);
-    });
+    } catch (...) {
+      std::lock_guard<std::mutex> g(mu);
+      if (!err) err = std::current_exception();
+      next.store(n);
+    }
+  };
+  std::vector<std::thread> pool;
+  for (int t = 1; t < nt; ++t) {
+    try {
+      pool.emplace_back(work);
+    } catch (...) {
+      break;  // fewer threads; the calling thread works too
+    }
+  }
+  work();
   for (auto &th : pool) th.join();
+  if (err) std::rethrow_exception(err);
 }
 
 void stage_cache(const jolt_cache_desc *desc, Staged *S, int threads) {
