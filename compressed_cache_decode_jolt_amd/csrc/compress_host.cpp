@@ -476,7 +476,8 @@ extern "C" jolt_status jolt_flash_layer_groups(const void *const *k_layers,
                                                double *align, jolt_stream stream) {
   return jolt::guarded("jolt_flash_layer_groups", [&]() -> jolt_status {
     std::string why;
-    if (!k_layers || !v_layers || !group_start || !n_groups || n_layers < 1 || max_group < 0)
+    if (!k_layers || !v_layers || !group_start || !n_groups || n_layers < 1 || max_group < 0 ||
+        std::isnan(tau))
       return set_error(JOLT_E_INVALID, "jolt_flash_layer_groups: bad arguments");
     for (int l = 0; l < n_layers; ++l)
       if (!check_shape(k_layers[l], x_dtype, 2, n_kv_heads, T, head_dim, p, &why) || !v_layers[l])

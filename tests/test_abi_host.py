@@ -157,3 +157,36 @@ def test_rope_domain_checked_before_launch():
 
 def test_long_context_rejected_at_load():
     expect(-2, J.jolt_load_cache, mutate(T=(1 << 20) + 1), 0, match="T=")
+
+
+def test_compressor_entry_points_validate_before_device_work():
+    """The compressor, grouping and quantiser entry points reject bad
+    arguments with JOLT_E_INVALID before touching any device pointer (the
+    pointers below are never dereferenced)."""
+    L = J.lib()
+    fake = C.c_void_p(0x1000)
+    P = _jolt.jolt_flash_params(64, 16, 2, 0)
+    out = (C.c_double * 200)()
+    n2 = C.c_double()
+    st = L.jolt_flash_spectra(fake, _jolt.JOLT_BF16, 1, 2, 128, 128, C.byref(_jolt.jolt_flash_params(0, 16, 2, 0)),
+                              out, out, C.addressof(n2), None)
+    assert st == -1 and b"flash params" in L.jolt_last_error()
+    st = L.jolt_flash_spectra(fake, _jolt.JOLT_BF16, 1, 2, 128, 129 + 127, C.byref(P), out, out,
+                              C.addressof(n2), None)
+    assert st == -1 and b"shape" in L.jolt_last_error()
+    st = L.jolt_flash_spectra(fake, _jolt.JOLT_BF16, 1, 2, 128, 128, C.byref(P), None, out,
+                              C.addressof(n2), None)
+    assert st == -1
+    # ranks: r_T above q_cap, r_T = 0 with r_F > 0, bits 3
+    for rT, rF, b in [(96, 32, 4), (0, 16, 0), (32, 16, 3)]:
+        st = L.jolt_flash_compress_cell(fake, _jolt.JOLT_BF16, 1, 2, 128, 128, C.byref(P), rT, rF, b,
+                                        C.c_uint64(1), _jolt.JOLT_BF16, fake, fake, fake, fake, fake, None)
+        assert st == -1, (rT, rF, b)
+    ks = (C.c_void_p * 2)(0x1000, 0x2000)
+    starts = (C.c_int32 * 3)()
+    ng = C.c_int32()
+    st = L.jolt_flash_layer_groups(ks, ks, _jolt.JOLT_BF16, 2, 2, 128, 128, C.byref(P),
+                                   C.c_double(float("nan")), 0, starts, C.byref(ng), None, None)
+    assert st == -1 and b"bad arguments" in L.jolt_last_error()
+    st = L.jolt_quantize_rows(fake, 4, 128, 3, fake, fake, None)
+    assert st == -1 and b"bits=3" in L.jolt_last_error()
