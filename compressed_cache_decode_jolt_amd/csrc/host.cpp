@@ -263,8 +263,23 @@ struct Plan {
   // of its own at byte tail_off of the workspace
   int tail_split, n_tsplit;
   size_t tail_off;
+  // one query per KV head with value ranks above 128 (key ranks up to 256):
+  // the value factors in a second pass over all heads (value2.hip), with the
+  // logits [batch][H][sc_stride] at sc_off, the merge's (max, sum) at st_off
+  // and the partial factor sums [batch][n2split][H][rV_max] at p2_off
+  bool v2;
+  int sc_stride, n2split, split2;
+  size_t sc_off, st_off, p2_off;
   size_t ws_bytes;
 };
+
+// A launch class that takes the second value pass: one query per KV head,
+// key ranks up to 256 and the 8-wave variant for value ranks above 128.
+// (The 4-wave classes for key ranks above 256 measured slower with it: their
+// split kernel does not get faster without the value factors.)
+static bool v2_class(int bK, int bV, int nkt, int nmv, bool hg1) {
+  return hg1 && nkt <= 8 && nmv > 8 && hg1_variant(bK, bV, nkt, 9);
+}
 
 // The MFMA kernel stages W2_K[h] = B_K G_K[h]^T / s and (with a key
 // residual) Pi in LDS as fp16 rows padded by 8 elements, next to 1 KiB of
@@ -328,7 +343,8 @@ static int cu_count() {
 }
 
 static jolt_status plan_decode(const jolt_cache *const *caches, int batch, int layer,
-                               const jolt_launch *launch, int tail_cap, Plan *p) {
+                               const jolt_launch *launch, int tail_cap, Plan *p,
+                               bool allow_v2 = true) {
   if (batch < 0) return fail(JOLT_E_INVALID, "batch=%d", batch);
   if (batch > 0 && !caches) return fail(JOLT_E_INVALID, "caches is NULL");
   const jolt_cache *c0 = batch ? caches[0] : nullptr;
@@ -412,6 +428,31 @@ static jolt_status plan_decode(const jolt_cache *const *caches, int batch, int l
     p->tail_off = rows * p->n_split * p->stride * sizeof(float);
     p->ws_bytes = p->tail_off + rows * p->n_tsplit * (4 + dd) * sizeof(float);
   }
+  // the second value pass, if a class of the call takes it
+  p->v2 = false;
+  p->sc_stride = p->n2split = p->split2 = 0;
+  p->sc_off = p->st_off = p->p2_off = 0;
+  if (allow_v2 && p->kernel == JOLT_KERNEL_MFMA && batch > 0 && c0->H == c0->H_q && c0->H <= 32) {
+    int t_pad = 0;
+    for (int b = 0; b < batch; ++b) {
+      const CellDev &k = caches[b]->h_layers[layer].c[0], &v = caches[b]->h_layers[layer].c[1];
+      if (v2_class(k.bits, v.bits, k.rT_pad / kRankPad, v.rT_pad / 16, true)) p->v2 = true;
+      t_pad = std::max(t_pad, caches[b]->h_layers[layer].T_pad);
+    }
+    if (p->v2) {
+      auto align = [](size_t x) { return (x + 255) / 256 * 256; };
+      const int H = c0->H, nb = std::min(batch, kMaxBatchPerLaunch);
+      // about one workgroup per compute unit over a chunk's sequences
+      const int want = std::max(1, (cu_count() + nb - 1) / nb);
+      p->split2 = round_up((p->T_max + want - 1) / want, 16);
+      p->n2split = (p->T_max + p->split2 - 1) / p->split2;
+      p->sc_stride = t_pad;
+      p->sc_off = align(p->ws_bytes);
+      p->st_off = align(p->sc_off + (size_t)batch * H * t_pad * sizeof(float));
+      p->p2_off = align(p->st_off + (size_t)batch * H * 2 * sizeof(float));
+      p->ws_bytes = p->p2_off + (size_t)batch * p->n2split * H * p->rV_max * sizeof(float);
+    }
+  }
   return JOLT_OK;
 }
 
@@ -451,9 +492,10 @@ static jolt_status decode_impl(const jolt_cache *const *caches, int32_t batch, i
                                const void *q, jolt_dtype q_dtype, const int32_t *q_pos,
                                const float *inv_freq, float softmax_scale, const TailIn &tail,
                                float *out, void *workspace, size_t ws_bytes,
-                               const jolt_launch *launch, jolt_stream stream) {
+                               const jolt_launch *launch, jolt_stream stream,
+                               bool allow_v2 = true) {
   Plan p;
-  jolt_status st = plan_decode(caches, batch, layer, launch, tail.cap, &p);
+  jolt_status st = plan_decode(caches, batch, layer, launch, tail.cap, &p, allow_v2);
   if (st != JOLT_OK) return st;
   if (batch == 0) return ok();
   if (!q || !q_pos || !inv_freq || !out) return fail(JOLT_E_INVALID, "NULL q/q_pos/inv_freq/out");
@@ -502,6 +544,21 @@ static jolt_status decode_impl(const jolt_cache *const *caches, int32_t batch, i
                                     : (const float *)((const uint8_t *)workspace + p.tail_off) +
                                           (size_t)b0 * c0->H_q * p.n_tsplit * (4 + c0->d);
     hipError_t e = hipSuccess;
+    // the second value pass of this chunk (sequences of the classes that take it)
+    V2Args v2;
+    std::memset(&v2, 0, sizeof v2);
+    if (p.v2) {
+      v2.scores = (const float *)((const uint8_t *)workspace + p.sc_off) + (size_t)b0 * c0->H * p.sc_stride;
+      v2.stats = (const float *)((const uint8_t *)workspace + p.st_off) + (size_t)b0 * c0->H * 2;
+      v2.part = (float *)((uint8_t *)workspace + p.p2_off) + (size_t)b0 * p.n2split * c0->H * p.rV_max;
+      v2.out = a.out;
+      v2.H = c0->H;
+      v2.d = c0->d;
+      v2.sc_stride = p.sc_stride;
+      v2.n2split = p.n2split;
+      v2.split2 = p.split2;
+      v2.rV_max = p.rV_max;
+    }
     // timing events: the first split launch's start and the last one's end
     KernelEvents ev;
     if (launch && b0 == 0) ev.begin = (hipEvent_t)launch->ev_begin;
@@ -536,7 +593,7 @@ static jolt_status decode_impl(const jolt_cache *const *caches, int32_t batch, i
         if (done[i0]) continue;
         const CellDev &k0 = caches[b0 + i0]->h_layers[layer].c[0];
         const CellDev &v0 = caches[b0 + i0]->h_layers[layer].c[1];
-        int n = 0, nkt = 0, rv = 0, lds = 0;
+        int n = 0, nkt = 0, rv = 0, lds = 0, lds2 = 0;
         for (int i = i0; i < nb; ++i) {
           const jolt_cache *c = caches[b0 + i];
           const CellDev &k = c->h_layers[layer].c[0], &v = c->h_layers[layer].c[1];
@@ -562,9 +619,28 @@ static jolt_status decode_impl(const jolt_cache *const *caches, int32_t batch, i
           nkt = k.rT_pad / kRankPad;
           rv = std::max(rv, v.rT_pad);
           lds = std::max(lds, mfma_lds_bytes(k, v, c->d, c->H_q == c->H));
+          // (the logits-out variant: 8 waves, no value-rank blocks)
+          lds2 = std::max(lds2, (int)mfma_lds_layout(c->d, nkt, k.bits > 0, 0, 8, true).total);
         }
         ma.nseq = n;
         ma.rV_max = rv;
+        const bool two = p.v2 && v2_class(k0.bits, v0.bits, nkt, rv / 16, c0->H_q == c0->H);
+        ma.scores = two ? (float *)v2.scores : nullptr;
+        ma.sc_stride = two ? p.sc_stride : 0;
+        if (two) {
+          lds = lds2;
+          for (int i = 0; i < n; ++i) {
+            const jolt_cache *c = caches[b0 + ma.seq[i].slot];
+            const CellDev &v = c->h_layers[layer].c[1];
+            if (v.rT_pad == 0) continue;  // no value factor: nothing for the second pass
+            SeqV2 &w = v2.seq[v2.nseq++];
+            w.A = v.A;
+            w.W2 = (const _Float16 *)v.W2;
+            w.T = c->T;
+            w.rT_pad = v.rT_pad;
+            w.slot = ma.seq[i].slot;
+          }
+        }
         // XCD-aware grid (all heads of a (sequence, split) unit on one XCD)
         ma.grid8 = (a.n_split & 7) == 0 ? 1 : ((n * a.n_split) & 7) == 0 ? 2 : 0;
         // frequency blocks of 16 whose angles stay below kRopeSmall for every
@@ -577,7 +653,8 @@ static jolt_status decode_impl(const jolt_cache *const *caches, int32_t batch, i
           for (int f = 16 * m; f < 16 * m + 16; ++f) w = std::max(w, (double)inv_freq[f]);
           if (w * (double)std::max(t_max - 1, 0) <= kRopeSmall) ma.rope_small |= 1 << m;
         }
-        if (i0 == last_class) ev.end = ev_last;
+        // (with a second value pass the end event goes to its last kernel)
+        if (i0 == last_class && !p.v2) ev.end = ev_last;
         e = jolt_launch_mfma(ma, n, k0.bits, v0.bits, nkt, lds, s, ev);
         if (e != hipSuccess) return fail(JOLT_E_HIP, "split kernel launch: %s", hipGetErrorString(e));
         ev.begin = nullptr;
@@ -634,8 +711,13 @@ static jolt_status decode_impl(const jolt_cache *const *caches, int32_t batch, i
       if (e != hipSuccess) return fail(JOLT_E_HIP, "tail kernel launch: %s", hipGetErrorString(e));
     }
     a.nseq = nb;
-    e = mfma ? jolt_launch_merge_outputs(a, nb, ws_splits, s) : jolt_launch_merge(a, nb, s);
+    e = mfma ? jolt_launch_merge_outputs(a, nb, ws_splits, s, p.v2 ? (float *)v2.stats : nullptr)
+             : jolt_launch_merge(a, nb, s);
     if (e != hipSuccess) return fail(JOLT_E_HIP, "merge kernel launch: %s", hipGetErrorString(e));
+    if (p.v2) {
+      e = jolt_launch_value2(v2, s, ev_last);
+      if (e != hipSuccess) return fail(JOLT_E_HIP, "value pass launch: %s", hipGetErrorString(e));
+    }
   }
   return ok();
 }
@@ -703,7 +785,9 @@ extern "C" jolt_status jolt_decode_attention_noalloc(const jolt_cache *const *ca
                                                      float softmax_scale, float *out,
                                                      const jolt_launch *launch, jolt_stream stream) {
   Plan p;
-  jolt_status st = plan_decode(caches, batch, layer, launch, 0, &p);
+  // (the value factors stay in the split kernel here: the second pass needs
+  // workspace for every token's logit)
+  jolt_status st = plan_decode(caches, batch, layer, launch, 0, &p, false);
   if (st != JOLT_OK) return st;
   if (p.ws_bytes > kScratchBytes)
     return fail(JOLT_E_WORKSPACE,
@@ -715,7 +799,7 @@ extern "C" jolt_status jolt_decode_attention_noalloc(const jolt_cache *const *ca
   st = scratch_address(&ws);
   if (st != JOLT_OK) return st;
   return decode_impl(caches, batch, layer, q, q_dtype, q_pos, inv_freq, softmax_scale, TailIn{},
-                     out, ws, kScratchBytes, launch, stream);
+                     out, ws, kScratchBytes, launch, stream, false);
 }
 
 // ----------------------------------------------------------------- dense --

@@ -122,6 +122,11 @@ struct MfmaArgs {
   // 1: fixed token-block schedule (wave w takes blocks w, w + waves, ...),
   // bitwise reproducible; 0: blocks claimed on demand
   int32_t fixed_blocks;
+  // one query per KV head, value factors in a second pass (the split kernel
+  // variant with SCO): every token's logit goes to scores[(slot H + h)
+  // sc_stride + t] and the split partials carry the residual part only
+  float *scores;
+  int32_t sc_stride;
   SeqMfma seq[kMaxBatchPerLaunch];
 };
 static_assert(sizeof(MfmaArgs) <= 4096, "MFMA kernel arguments exceed 4 KiB");
@@ -150,6 +155,23 @@ struct DenseArgs {
   int32_t q_pos[kMaxBatchPerLaunch];
   int32_t T_seq[kMaxBatchPerLaunch];  // tokens of each sequence (<= T) that are attended to
   int32_t seq0;           // first sequence of this launch
+};
+
+// Second pass of the value factors for one query per KV head (value_gemm /
+// value_finish): a[h] = sum_t exp(s[h, t] - m*[h]) A_V[t] over all heads at
+// once, then out[h] += W2_V[h] a[h] / L*[h].
+struct SeqV2 {
+  const void *A;         // A_V, fp16 (A_V s), 16 x 16 tiles (av_index layout)
+  const _Float16 *W2;    // W2_V [H][d][rT_pad] fp16
+  int32_t T, rT_pad, slot, pad_;
+};
+struct V2Args {
+  const float *scores;   // logits [slot][H][sc_stride]
+  const float *stats;    // (m*, L*) [slot][H][2] from the merge
+  float *part;           // [slot][n2split][H][rV_max] partial a
+  float *out;            // [slot][H][d], the merge's output, a-part added
+  int32_t H, d, sc_stride, n2split, split2, rV_max, nseq;
+  SeqV2 seq[kMaxBatchPerLaunch];
 };
 
 }  // namespace jolt
@@ -217,7 +239,11 @@ hipError_t jolt_launch_generic(const jolt::DecodeArgs &a, int nseq, hipStream_t 
 hipError_t jolt_launch_mfma(const jolt::MfmaArgs &a, int nseq, int bK, int bV, int nkt,
                             int lds_bytes, hipStream_t s, jolt::KernelEvents ev);
 hipError_t jolt_launch_merge(const jolt::DecodeArgs &a, int nseq, hipStream_t s);
-hipError_t jolt_launch_merge_outputs(const jolt::DecodeArgs &a, int nseq, int ns, hipStream_t s);
+// stats (may be NULL): (max, sum of weights) per (sequence, query head)
+hipError_t jolt_launch_merge_outputs(const jolt::DecodeArgs &a, int nseq, int ns, hipStream_t s,
+                                     float *stats = nullptr);
+// end (may be NULL): set to the end time of the pass's last kernel
+hipError_t jolt_launch_value2(const jolt::V2Args &a, hipStream_t s, hipEvent_t end);
 hipError_t jolt_launch_dense(const jolt::DenseArgs &a, int nseq, hipStream_t s);
 hipError_t jolt_launch_dense_merge(const jolt::DenseArgs &a, int nseq, hipStream_t s);
 hipError_t jolt_launch_unpack(const jolt::LayerDev *layer, int tau, int H, int T, int d,

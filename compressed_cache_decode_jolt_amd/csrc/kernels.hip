@@ -692,7 +692,7 @@ __global__ __launch_bounds__(256, 2) void dense_mfma(DenseArgs a) {
 // w_s = exp(m_s - max m).  The first 32 splits' columns are fetched together
 // with m and l, so short reductions take one memory round trip.
 __global__ __launch_bounds__(256) void merge_outputs(const float *ws, float *out, int ns, int d,
-                                                     int H_q) {
+                                                     int H_q, float *stats) {
   const int j = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int st = 4 + d, f = tid & 127, part = tid >> 7;
   const float *pb = ws + ((size_t)(b * H_q + j) * ns) * st;
@@ -742,6 +742,10 @@ __global__ __launch_bounds__(256) void merge_outputs(const float *ws, float *out
   if (part == 1 && f < d) half_s[f] = acc;
   __syncthreads();
   if (part == 0 && f < d) out[((size_t)b * H_q + j) * d + f] = (acc + half_s[f]) / ls;
+  if (stats && tid == 0) {
+    stats[((size_t)b * H_q + j) * 2] = mx;
+    stats[((size_t)b * H_q + j) * 2 + 1] = ls;
+  }
 }
 
 // ------------------------------------------------------------- unpack --
@@ -839,15 +843,16 @@ hipError_t jolt_launch_dense(const DenseArgs &a, int nseq, hipStream_t s) {
 
 hipError_t jolt_launch_dense_merge(const DenseArgs &a, int nseq, hipStream_t s) {
   hipLaunchKernelGGL(merge_outputs, dim3(a.H_q, nseq), dim3(256), 0, s, (const float *)a.ws, a.out,
-                     a.ws_splits, a.d, a.H_q);
+                     a.ws_splits, a.d, a.H_q, (float *)nullptr);
   return hipGetLastError();
 }
 
 // ns: splits per (sequence, query head) row of the workspace (the split
 // kernel's plus any uncompressed-tail splits)
-hipError_t jolt_launch_merge_outputs(const DecodeArgs &a, int nseq, int ns, hipStream_t s) {
+hipError_t jolt_launch_merge_outputs(const DecodeArgs &a, int nseq, int ns, hipStream_t s,
+                                     float *stats) {
   hipLaunchKernelGGL(merge_outputs, dim3(a.H_q, nseq), dim3(256), 0, s, (const float *)a.ws, a.out,
-                     ns, a.d, a.H_q);
+                     ns, a.d, a.H_q, stats);
   return hipGetLastError();
 }
 
