@@ -72,13 +72,40 @@ def window_mean(trace, match, start, count):
     return sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in sel) / count / 1e3
 
 
+def call_window_mean(trace, start, count, first="decode_mfma", last="value_finish",
+                     kernels=("decode_mfma", "merge_outputs", "value_gemm", "value_finish")):
+    """Mean span (us) of layer calls start .. start+count-1 of a --kernel-trace
+    CSV: a call is a run of ``first`` dispatches and the kernels after it up
+    to the next ``first``; its span runs from its first dispatch's start to
+    the end of its ``last`` dispatch if it has one, else of its last
+    ``first`` dispatch -- what the library's timing events bracket."""
+    rows = [r for r in csv.DictReader(open(trace)) if any(k in r["Kernel_Name"] for k in kernels)]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    calls, cur, prev_first = [], None, False
+    for r in rows:
+        is_first = first in r["Kernel_Name"]
+        if is_first and not prev_first:
+            cur = {"start": int(r["Start_Timestamp"]), "end_first": 0, "end_last": None}
+            calls.append(cur)
+        if cur is None:
+            continue
+        if is_first:
+            cur["end_first"] = max(cur["end_first"], int(r["End_Timestamp"]))
+        elif last in r["Kernel_Name"]:
+            cur["end_last"] = int(r["End_Timestamp"])
+        prev_first = is_first
+    sel = calls[start:start + count]
+    assert len(sel) == count, f"only {len(calls)} calls"
+    return sum(((c["end_last"] or c["end_first"]) - c["start"]) for c in sel) / count / 1e3
+
+
 def counter_per_dispatch(path, counter, match=None):
     """{kernel name: [value per dispatch]} for one counter of a --pmc CSV."""
     acc = {}
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] != counter:
             continue
-        if match and match not in r["Kernel_Name"]:
+        if match and not any(m in r["Kernel_Name"] for m in match.split("|")):
             continue
         key = (r["Kernel_Name"], r["Dispatch_Id"])
         acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
@@ -104,9 +131,16 @@ def traffic(args):
     assert fetch and write, f"no dispatch of a kernel matching {args.kernel!r}"
     fv = [x for v in fetch.values() for x in v]
     wv = [x for v in write.values() for x in v]
-    # a launch (one layer call) may run several launch classes, i.e. dispatches
+    # a launch (one layer call) may run several launch classes, i.e.
+    # dispatches of the anchor kernel (the first of --kernel's alternatives),
+    # and other kernels (a second value pass): bytes per launch = all
+    # matching dispatches' bytes / launches, launches = anchor dispatches /
+    # dispatches per launch
     per = getattr(args, "dispatches_per_launch", 1.0) or 1.0
-    fb, wb = per * ff * sum(fv) / len(fv), per * wf * sum(wv) / len(wv)
+    anchor = args.kernel.split("|")[0]
+    nf = sum(len(v) for k, v in fetch.items() if anchor in k) / per
+    nw = sum(len(v) for k, v in write.items() if anchor in k) / per
+    fb, wb = ff * sum(fv) / nf, wf * sum(wv) / nw
     rec = {"kernel_hash": kernel_hash(), "bytes_per_launch": fb + wb,
            "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
            "dispatches": [len(fv), len(wv)], "dispatches_per_launch": per,
@@ -126,10 +160,10 @@ def traffic(args):
                      f"{args.copy_bytes:,}", f"{fraw:,.0f}", ff),
                  "| copy of %s B: WRITE_SIZE | %s (=> %.1f B per unit) |" % (
                      f"{args.copy_bytes:,}", f"{wraw:,.0f}", wf),
-                 "| `%s` FETCH_SIZE x factor | %s B per launch (%d dispatches, %.3g per launch) |" % (
-                     args.kernel, f"{fb:,.0f}", len(fv), per),
-                 "| `%s` WRITE_SIZE x factor | %s B per launch (%d dispatches, %.3g per launch) |" % (
-                     args.kernel, f"{wb:,.0f}", len(wv), per),
+                 "| `%s` FETCH_SIZE x factor | %s B per launch (%d dispatches, %.3g of `%s` per launch) |" % (
+                     args.kernel, f"{fb:,.0f}", len(fv), per, anchor),
+                 "| `%s` WRITE_SIZE x factor | %s B per launch (%d dispatches, %.3g of `%s` per launch) |" % (
+                     args.kernel, f"{wb:,.0f}", len(wv), per, anchor),
                  "| HBM traffic per launch | %s B |" % f"{fb + wb:,.0f}"]
         if args.alg_bytes:
             lines += ["| algorithmic bytes per launch | %s B |" % f"{args.alg_bytes:,.0f}",
@@ -190,6 +224,9 @@ def main():
     s.add_argument("--trace", default=None, help="kernel-trace CSV for --window")
     s.add_argument("--window", nargs=3, metavar=("KERNEL", "START", "COUNT"), default=None,
                    help="also report the mean duration of these dispatches of KERNEL")
+    s.add_argument("--call-window", nargs=2, type=int, metavar=("START", "COUNT"), default=None,
+                   help="also report the mean span of these layer calls (split kernels to "
+                        "the end of the second value pass)")
     t = sub.add_parser("traffic")
     for k in ("workload", "kernel", "fetch", "write", "calib_fetch", "calib_write", "out"):
         t.add_argument("--" + k.replace("_", "-"), required=True)
@@ -218,6 +255,11 @@ def main():
             k, st, n = a.window[0], int(a.window[1]), int(a.window[2])
             text += ("\nMean duration of `%s` dispatches %d-%d (in start order): %.2f us\n"
                      % (k, st, st + n - 1, window_mean(a.trace, k, st, n)))
+        if a.call_window:
+            st, n = a.call_window
+            text += ("\nMean span of layer calls %d-%d (first split-kernel start to the end of the "
+                     "call's last split kernel, or of its second value pass): %.2f us\n"
+                     % (st, st + n - 1, call_window_mean(a.trace, st, n)))
         text += "\nKernel sources hash: `%s`\n" % kernel_hash()
         open(a.out, "w").write(text)
         print(text)

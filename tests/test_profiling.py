@@ -73,3 +73,38 @@ def test_counters_table_means_per_dispatch_and_ratios(tmp_path):
     cells = [c.strip() for c in t[2].strip("|").split("|")]
     # busy: (200 + 400) / 2 = 300; mfma: (50 + 250) / 2 = 150; ratio 0.5
     assert cells[1] == "2" and cells[2] == "300" and cells[3] == "150" and cells[4] == "0.500"
+
+
+def test_call_window_spans_split_kernels_and_the_value_pass(tmp_path):
+    # call 1: two split launches, merge, value pass; call 2: one split launch
+    # and merge only (no value pass); call 3: split, merge, value pass
+    rows = [("decode_mfma<a>", 100, 150), ("decode_mfma<b>", 150, 190), ("merge_outputs", 190, 195),
+            ("value_gemm", 195, 230), ("value_finish", 230, 250),
+            ("decode_mfma<a>", 300, 340), ("merge_outputs", 340, 345), ("other", 350, 900),
+            ("decode_mfma<a>", 1000, 1040), ("merge_outputs", 1040, 1045), ("value_gemm", 1045, 1060),
+            ("value_finish", 1060, 1070)]
+    p = _write(tmp_path / "trace.csv", ["Kernel_Name", "Start_Timestamp", "End_Timestamp"], rows)
+    # spans: 250 - 100, 340 - 300, 1070 - 1000 ns
+    assert P.call_window_mean(p, 0, 3) == pytest.approx((150 + 40 + 70) / 3 / 1e3)
+    assert P.call_window_mean(p, 1, 1) == pytest.approx(40e-3)
+
+
+def test_traffic_per_launch_counts_every_kernel_of_a_call(tmp_path):
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    cf = _write(tmp_path / "cf.csv", hdr, [(1, "copy", "FETCH_SIZE", 1024)])
+    cw = _write(tmp_path / "cw.csv", hdr, [(1, "copy", "WRITE_SIZE", 1024)])
+    # two layer calls: decode + value pass, decode alone
+    kf = _write(tmp_path / "kf.csv", hdr, [(1, "decode_mfma<x>", "FETCH_SIZE", 10),
+                                           (2, "value_gemm", "FETCH_SIZE", 6),
+                                           (3, "value_finish", "FETCH_SIZE", 2),
+                                           (4, "decode_mfma<y>", "FETCH_SIZE", 30)])
+    kw = _write(tmp_path / "kw.csv", hdr, [(1, "decode_mfma<x>", "WRITE_SIZE", 4),
+                                           (4, "decode_mfma<y>", "WRITE_SIZE", 4)])
+    out = tmp_path / "traffic.json"
+    a = types.SimpleNamespace(calib_fetch=cf, calib_write=cw, fetch=kf, write=kw,
+                              kernel="decode_mfma|value_gemm|value_finish", copy_bytes=1024,
+                              out=str(out), workload="w", name="decode_mfma", dispatches_per_launch=1.0)
+    P.traffic(a)
+    rec = json.load(open(out))["w/decode_mfma"]
+    assert rec["fetch_bytes_per_launch"] == pytest.approx((10 + 6 + 2 + 30) / 2)
+    assert rec["write_bytes_per_launch"] == pytest.approx(4.0)
