@@ -6,7 +6,9 @@ Against the oracle's decode of the same caches, at the MFMA tolerances
 (rel-L2 <= 5e-3, max-abs <= 2e-2):
 
 * one launch class whose sequences have different value ranks, one of them
-  0 (no value factor: the second pass skips it) and ragged lengths;
+  0 (no value factor: the second pass skips it) and ragged lengths, with
+  short splits and with splits of 1024 tokens (two 16-token blocks per wave
+  step in the split kernel);
 * more than 32 sequences (two batch chunks: the logits, statistics and
   partial sums at the second chunk's offsets);
 * an uncompressed tail under the same softmax;
@@ -37,7 +39,7 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
 
 
-def decode(caches, q, q_pos, inv, scale, deterministic=False, noalloc=False):
+def decode(caches, q, q_pos, inv, scale, deterministic=False, noalloc=False, split=0):
     hs = [J.jolt_load_cache(c) for c in caches]
     qt = torch.from_numpy(q.astype(np.float32)).to(torch.bfloat16).cuda()
     out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
@@ -45,10 +47,10 @@ def decode(caches, q, q_pos, inv, scale, deterministic=False, noalloc=False):
         J.jolt_decode_attention_noalloc(hs, 0, qt, q_pos, inv, scale, out, kernel=J.KERNEL_MFMA,
                                         deterministic=deterministic)
     else:
-        nb = J.jolt_decode_workspace_size(hs, 0, kernel=J.KERNEL_MFMA)
+        nb = J.jolt_decode_workspace_size(hs, 0, kernel=J.KERNEL_MFMA, split_tokens=split)
         ws = torch.full((nb,), 0x7F, dtype=torch.uint8, device="cuda")  # no zeroed buffers
         J.jolt_decode_attention(hs, 0, qt, q_pos, inv, scale, out, ws, kernel=J.KERNEL_MFMA,
-                                deterministic=deterministic)
+                                split_tokens=split, deterministic=deterministic)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64)
 
@@ -60,7 +62,8 @@ def check(got, caches, q, q_pos, inv, scale):
         assert r <= 5e-3 and mx <= 2e-2, (b, r, mx)
 
 
-def test_class_with_mixed_value_ranks():
+@pytest.mark.parametrize("split", [0, 1024])
+def test_class_with_mixed_value_ranks(split):
     d, H = 128, 4
     # same key bits, key rank and value bits: one launch class; value ranks
     # 400, 0, 160, 288
@@ -71,7 +74,7 @@ def test_class_with_mixed_value_ranks():
     inv = gen.rope_inv_freq_input(1e4, d)
     q = np.stack([gen.queries(301, i, 0, H, d, "bf16") for i in range(len(spec))])
     q_pos = [T for T, _, _ in spec]
-    check(decode(caches, q, q_pos, inv, 0.088), caches, q, q_pos, inv, 0.088)
+    check(decode(caches, q, q_pos, inv, 0.088, split=split), caches, q, q_pos, inv, 0.088)
 
 
 def test_two_batch_chunks():
