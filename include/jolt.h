@@ -98,7 +98,9 @@ typedef struct {
   void *ev_end;          /* start time of the first split-T kernel launch of the  */
                          /* call / the end time of its last one (kernel           */
                          /* timestamps, not stream markers), so a caller can time */
-                         /* the split-T kernels alone                             */
+                         /* the split-T kernels alone; where the call has a       */
+                         /* second value pass (one query per KV head, value ranks */
+                         /* above 128) the end is that pass's last kernel's       */
   int32_t deterministic; /* 1: fixed assignment of token blocks to waves, so two  */
                          /* calls with the same inputs and settings give the same */
                          /* output bits (the Reproducibility Statement of the     */
@@ -131,7 +133,9 @@ jolt_status jolt_cache_info(const jolt_cache *cache, int32_t *n_layers, int32_t 
                             size_t *device_bytes);
 
 /* Workspace bytes jolt_decode_attention needs for these caches, layer and
- * launch settings (launch may be NULL). */
+ * launch settings (launch may be NULL): the split partials and, where a class
+ * of the call takes the second value pass, every token's logit, the softmax
+ * statistics and the partial value-factor sums. */
 jolt_status jolt_decode_workspace_size(const jolt_cache *const *caches, int32_t batch,
                                        int32_t layer, const jolt_launch *launch, size_t *bytes);
 
