@@ -14,7 +14,9 @@ Against the oracle's decode of the same caches, at the MFMA tolerances
 * an uncompressed tail under the same softmax;
 * the fixed block schedule (bitwise repeatable through both passes);
 * the allocation-free entry point, which keeps the single pass, against the
-  workspace entry point on the same call.
+  workspace entry point on the same call;
+* 20 KV heads (a partly empty second 16-head group) and 40 (above the pass's
+  32: the single pass).
 """
 import numpy as np
 import pytest
@@ -142,3 +144,18 @@ def test_fixed_schedule_is_bitwise_repeatable_and_noalloc_agrees():
     c = decode(caches, q, q_pos, inv, 0.088, noalloc=True)
     check(c, caches, q, q_pos, inv, 0.088)
     assert rel_l2(c, a) <= 5e-3
+
+
+@pytest.mark.parametrize("H", [20, 40])
+def test_head_counts_around_the_two_head_groups(H):
+    """20 KV heads: the second 16-head group of the value product is partly
+    empty; 40 heads: more than the pass's 32, so the call keeps the single
+    pass.  Either way the oracle's result."""
+    d = 128
+    spec = [(600, (96, 64, 4), (224, 64, 2)), (1000, (96, 48, 4), (160, 48, 2))]
+    caches = [gen.small_cache(700 + 10 * H + i, T, H, H, d, [(aK, aV)], [1])
+              for i, (T, aK, aV) in enumerate(spec)]
+    inv = gen.rope_inv_freq_input(1e4, d)
+    q = np.stack([gen.queries(701, i, 0, H, d, "bf16") for i in range(len(spec))])
+    q_pos = [T for T, _, _ in spec]
+    check(decode(caches, q, q_pos, inv, 0.088), caches, q, q_pos, inv, 0.088)
