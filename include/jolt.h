@@ -133,16 +133,26 @@ jolt_status jolt_cache_info(const jolt_cache *cache, int32_t *n_layers, int32_t 
                             size_t *device_bytes);
 
 /* Workspace bytes jolt_decode_attention needs for these caches, layer and
- * launch settings (launch may be NULL): the split partials and, where a class
- * of the call takes the second value pass, every token's logit, the softmax
- * statistics and the partial value-factor sums. */
+ * launch settings (launch may be NULL): the split partials (each a partial
+ * softmax state of the fused kernel that "A JoLT for the KV cache" §4.5
+ * describes: running max, weight sum and weighted value sum of one token
+ * range) and, where a class of the call takes the second value pass, every
+ * token's logit, the softmax statistics and the partial value-factor sums.
+ * Errors: JOLT_E_INVALID (NULL pointers, batch < 0, layer out of range,
+ * handles with different shapes, launch fields out of range),
+ * JOLT_E_UNSUPPORTED (kernel forced to MFMA for a cache it cannot run). */
 jolt_status jolt_decode_workspace_size(const jolt_cache *const *caches, int32_t batch,
                                        int32_t layer, const jolt_launch *launch, size_t *bytes);
 
 /*
  * Decode attention of one layer for a batch of sequences, each with its own
  * cache handle (handles in one call share n_layers, groups, heads and d; T
- * and the per-cell ranks and bits may differ).
+ * and the per-cell ranks and bits may differ).  This is the operation of
+ * "A JoLT for the KV cache" §4.5 (and the Abstract): attention for one new
+ * query per head evaluated over the stored factors and packed residuals,
+ * with key tiles rebuilt and rotated at their positions (RoPE does not
+ * commute with the factorisation, §5) and values taken in factor space; the
+ * result is the formula in this file's header.
  *   q         DEVICE [batch][n_q_heads][d], pre-RoPE, q_dtype (F32 or BF16)
  *   q_pos     HOST   [batch] query positions (normally the cache's T), in
  *             [0, 2^20]
