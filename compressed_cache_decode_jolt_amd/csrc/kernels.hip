@@ -24,6 +24,7 @@ using namespace jolt;
 namespace {
 
 constexpr int kTT = 32;  // tokens per generic tile
+constexpr int kGenStage = kMaxD * (kMaxD + 2);  // floats of LDS for the generic kernel's key-side matrices
 constexpr int kMergeChunk = 2048;
 
 __device__ inline float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -91,6 +92,13 @@ __global__ __launch_bounds__(256) void decode_generic(DecodeArgs a) {
   __shared__ float S[kMaxHg][kTT];
   __shared__ float cacc[kMaxHg][kMaxD];
   __shared__ float m_s[kMaxHg], l_s[kMaxHg], al_s[kMaxHg];
+  // The key-side matrices every tile reads, staged once per workgroup as
+  // float: Pi (b_K > 0), then B_K and G_K[h] where they still fit (read from
+  // memory otherwise).  Each key element reads a whole row of them, so from
+  // memory the tile loop waits on one load per multiply-add.  Rows carry one
+  // float of padding: the threads of a wave read different rows at the same
+  // column, which would otherwise all fall on one LDS bank.
+  __shared__ float stage[kGenStage];
 
   float *part0 = a.ws + ((size_t)(b * a.H_q + h * Hg) * a.n_split + split) * a.stride;
   const size_t ustride = (size_t)a.n_split * a.stride;
@@ -120,18 +128,42 @@ __global__ __launch_bounds__(256) void decode_generic(DecodeArgs a) {
   }
   for (int x = tid; x < Hg * V.rT_pad; x += 256)
     part0[(x / V.rT_pad) * ustride + 4 + (x % V.rT_pad)] = 0.0f;
+  const int sPi = d + 1, sB = K.rF + 1, sG = K.rT + 1;  // staged row strides
+  const int nPi = K.bits ? d * sPi : 0, nB = d * sB, nG = K.rF * sG;
+  const bool bL = nPi + nB <= kGenStage, gL = bL && nPi + nB + nG <= kGenStage;
+  float *const Pis = stage, *const Bs = stage + nPi, *const Gs = stage + nPi + nB;
+  if (K.bits)
+    for (int x = tid; x < d * d; x += 256) Pis[(x / d) * sPi + x % d] = L.Pi[x];
+  if (bL)
+    for (int x = tid; x < d * K.rF; x += 256)
+      Bs[(x / K.rF) * sB + x % K.rF] = ldf<F32>(K.B, (size_t)(x / K.rF) * K.rF_pad + x % K.rF);
+  if (gL)
+    for (int x = tid; x < K.rF * K.rT; x += 256)
+      Gs[(x / K.rT) * sG + x % K.rT] = ldf<F32>(K.G, ((size_t)h * K.rF_pad + x / K.rT) * K.rT_pad + x % K.rT);
   __syncthreads();
 
   const float Lk = 0.5f * (float)((1 << K.bits) - 1);
   for (int tt = t0; tt < t1; tt += kTT) {
     const int nt = min(kTT, t1 - tt);
+    // the tile's A_K rows, staged in Kt (written only after P) when they fit
+    const bool aL = gL && K.rT <= kMaxD;
+    if (aL) {
+      for (int x = tid; x < nt * K.rT; x += 256)
+        Kt[x / K.rT][x % K.rT] = ldAk<F32>(K, (size_t)(tt + x / K.rT) * K.rT_pad + x % K.rT);
+      __syncthreads();
+    }
     // P = A_K[t] G_K  (t < nt, j < r_F)
     for (int x = tid; x < nt * K.rF; x += 256) {
       int t = x / K.rF, j = x % K.rF;
       float acc = 0.0f;
-      for (int r = 0; r < K.rT; ++r)
-        acc += ldAk<F32>(K, (size_t)(tt + t) * K.rT_pad + r) *
-               ldf<F32>(K.G, ((size_t)h * K.rF_pad + j) * K.rT_pad + r);
+      if (aL)
+        for (int r = 0; r < K.rT; ++r) acc += Kt[t][r] * Gs[j * sG + r];
+      else if (gL)
+        for (int r = 0; r < K.rT; ++r) acc += ldAk<F32>(K, (size_t)(tt + t) * K.rT_pad + r) * Gs[j * sG + r];
+      else
+        for (int r = 0; r < K.rT; ++r)
+          acc += ldAk<F32>(K, (size_t)(tt + t) * K.rT_pad + r) *
+                 ldf<F32>(K.G, ((size_t)h * K.rF_pad + j) * K.rT_pad + r);
       P[t][j] = acc;
     }
     // key residual in the rotated basis
@@ -146,9 +178,12 @@ __global__ __launch_bounds__(256) void decode_generic(DecodeArgs a) {
     for (int x = tid; x < nt * d; x += 256) {
       int t = x / d, f = x % d;
       float acc = 0.0f;
-      for (int j = 0; j < K.rF; ++j) acc += P[t][j] * ldf<F32>(K.B, (size_t)f * K.rF_pad + j);
+      if (bL)
+        for (int j = 0; j < K.rF; ++j) acc += P[t][j] * Bs[f * sB + j];
+      else
+        for (int j = 0; j < K.rF; ++j) acc += P[t][j] * ldf<F32>(K.B, (size_t)f * K.rF_pad + j);
       if (K.bits)
-        for (int i = 0; i < d; ++i) acc += X[t][i] * L.Pi[(size_t)f * d + i];
+        for (int i = 0; i < d; ++i) acc += X[t][i] * Pis[f * sPi + i];
       Kt[t][f] = acc;
     }
     __syncthreads();
@@ -177,6 +212,11 @@ __global__ __launch_bounds__(256) void decode_generic(DecodeArgs a) {
         X[t][i] = ((float)v_code(V, h, tt + t, i, T_pad, d) - Lv) *
                   V.scales[(size_t)h * T_pad + tt + t];
       }
+    // the tile's A_V rows, staged in P (no longer read) when they fit
+    const bool avL = V.rT <= kMaxD;
+    if (avL)
+      for (int x = tid; x < nt * V.rT; x += 256)
+        P[x / V.rT][x % V.rT] = ldAk<F32>(V, av_index(tt + x / V.rT, x % V.rT, V.rT_pad));
     // online softmax
     if (tid < Hg) {
       int u = tid;
@@ -205,10 +245,10 @@ __global__ __launch_bounds__(256) void decode_generic(DecodeArgs a) {
     for (int x = tid; x < Hg * V.rT; x += 256) {
       int u = x / V.rT, r = x % V.rT;
       float acc = 0.0f;
-      for (int t = 0; t < nt; ++t) {
-        int tg = tt + t;
-        acc += S[u][t] * ldAk<F32>(V, av_index(tg, r, V.rT_pad));
-      }
+      if (avL)
+        for (int t = 0; t < nt; ++t) acc += S[u][t] * P[t][r];
+      else
+        for (int t = 0; t < nt; ++t) acc += S[u][t] * ldAk<F32>(V, av_index(tt + t, r, V.rT_pad));
       float *pa = part0 + u * ustride + 4 + r;
       *pa = al_s[u] * *pa + acc;
     }
