@@ -273,12 +273,14 @@ struct Plan {
   size_t ws_bytes;
 };
 
-// A launch class that takes the second value pass: one query per KV head,
-// key ranks up to 256 and the 8-wave variant for value ranks above 128.
-// (The 4-wave classes for key ranks above 256 measured slower with it: their
-// split kernel does not get faster without the value factors.)
+// A launch class that takes the second value pass: one query per KV head
+// and a value factor, with key ranks up to 256 and value ranks above 128
+// (the 8-wave variant), or key ranks above 256 where W2_K and Pi fit in the
+// LDS at 8 waves.  (At 4 waves the wide classes measured slower with it:
+// their split kernel did not get faster without the value factors.)
 static bool v2_class(int bK, int bV, int nkt, int nmv, bool hg1) {
-  return hg1 && nkt <= 8 && nmv > 8 && hg1_variant(bK, bV, nkt, 9);
+  if (!hg1 || nmv == 0) return false;
+  return nkt <= 8 ? nmv > 8 && hg1_variant(bK, bV, nkt, 9) : wide_sco(bK, nkt);
 }
 
 // The MFMA kernel stages W2_K[h] = B_K G_K[h]^T / s and (with a key

@@ -32,6 +32,14 @@ __host__ __device__ constexpr bool hg1_variant(int bK, int bV, int kt, int nmv) 
   return kt > 8 || (nmv > 8 && !(bK == 8 && bV == 8 && kt == 8));
 }
 
+// One query per KV head with key ranks above 256 (kt > 8) and value ranks
+// above 128: the logits-out variant (the value factors in a second pass over
+// all heads) runs 8 waves with Pi in LDS where W2_K and Pi fit there -- d =
+// 128; with a key residual that is key ranks up to 448.
+__host__ __device__ constexpr bool wide_sco(int bK, int kt) {
+  return kt > 8 && mfma_lds_layout(128, kt, bK > 0, 0, 8, true).total <= 160u * 1024u;
+}
+
 struct CellDev {
   // K: A [T_pad][rT_pad] row-major (fp16, scaled, for bf16 caches).
   // V: A in the av_index layout (factor dtype).

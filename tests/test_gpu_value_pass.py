@@ -16,7 +16,11 @@ Against the oracle's decode of the same caches, at the MFMA tolerances
 * the allocation-free entry point, which keeps the single pass, against the
   workspace entry point on the same call;
 * 20 KV heads (a partly empty second 16-head group) and 40 (above the pass's
-  32: the single pass).
+  32: the single pass);
+* key ranks above 256: 8 waves with Pi in LDS where W2_K and Pi fit there
+  (ranks 320 without a key residual, 384 and 448 with one; any value rank,
+  and a sequence without a value factor in the same launch), the 4-wave
+  single pass where they do not (rank 512 with 8-bit keys).
 """
 import numpy as np
 import pytest
@@ -159,3 +163,19 @@ def test_head_counts_around_the_two_head_groups(H):
     q = np.stack([gen.queries(701, i, 0, H, d, "bf16") for i in range(len(spec))])
     q_pos = [T for T, _, _ in spec]
     check(decode(caches, q, q_pos, inv, 0.088), caches, q, q_pos, inv, 0.088)
+
+
+@pytest.mark.parametrize("aK, aV", [((320, 96, 0), (256, 32, 4)), ((384, 32, 2), (192, 96, 8)),
+                                    ((448, 64, 4), (160, 64, 2)), ((448, 64, 4), (64, 32, 2)),
+                                    ((384, 32, 8), (32, 16, 4)), ((512, 96, 8), (224, 48, 4))])
+def test_wide_key_ranks(aK, aV):
+    d, H = 128, 4
+    rv2 = aV[0] - 32  # the second sequence's value rank (0: no value factor)
+    spec = [(1400, aK, aV), (700, (aK[0], aK[1] // 2, aK[2]), (rv2, aV[1] if rv2 else 0, aV[2]))]
+    caches = [gen.small_cache(800 + aK[0] + i, T, H, H, d, [(k, v)], [1])
+              for i, (T, k, v) in enumerate(spec)]
+    inv = gen.rope_inv_freq_input(1e4, d)
+    q = np.stack([gen.queries(801, i, 0, H, d, "bf16") for i in range(len(spec))])
+    q_pos = [T for T, _, _ in spec]
+    check(decode(caches, q, q_pos, inv, 0.088), caches, q, q_pos, inv, 0.088)
+    check(decode(caches, q, q_pos, inv, 0.088, split=512), caches, q, q_pos, inv, 0.088)
