@@ -41,7 +41,8 @@ __host__ __device__ constexpr bool wide_sco(int bK, int kt) {
 }
 
 struct CellDev {
-  // K: A [T_pad][rT_pad] row-major (fp16, scaled, for bf16 caches).
+  // K: A [T_pad][rT_pad] in MFMA operand fragments (ak_index layout; fp16,
+  // scaled, for bf16 caches).
   // V: A in the av_index layout (factor dtype).
   const void *A;
   // K: G^T of this layer, [H][rF_pad][rT_pad].  V: G of this layer,
@@ -63,7 +64,7 @@ struct CellDev {
   const float *scales;    // this layer: [H][T_pad]
   int32_t rT, rF, bits, rT_pad, rF_pad;
   // Keys of bf16 caches store A as fp16(A * s) with s a power of two (so
-  // the MFMA key tile reads A_K rows as they are; W2_K holds B G^T / s);
+  // the MFMA key tile reads A_K fragments as they are; W2_K holds B G^T / s);
   // a_inv = 1 / s (1 elsewhere).
   float a_inv;
 };

@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void decode_generic(DecodeArgs a) {
     const bool aL = gL && K.rT <= kMaxD;
     if (aL) {
       for (int x = tid; x < nt * K.rT; x += 256)
-        Kt[x / K.rT][x % K.rT] = ldAk<F32>(K, (size_t)(tt + x / K.rT) * K.rT_pad + x % K.rT);
+        Kt[x / K.rT][x % K.rT] = ldAk<F32>(K, ak_index(tt + x / K.rT, x % K.rT, K.rT_pad));
       __syncthreads();
     }
     // P = A_K[t] G_K  (t < nt, j < r_F)
@@ -159,10 +159,10 @@ __global__ __launch_bounds__(256) void decode_generic(DecodeArgs a) {
       if (aL)
         for (int r = 0; r < K.rT; ++r) acc += Kt[t][r] * Gs[j * sG + r];
       else if (gL)
-        for (int r = 0; r < K.rT; ++r) acc += ldAk<F32>(K, (size_t)(tt + t) * K.rT_pad + r) * Gs[j * sG + r];
+        for (int r = 0; r < K.rT; ++r) acc += ldAk<F32>(K, ak_index(tt + t, r, K.rT_pad)) * Gs[j * sG + r];
       else
         for (int r = 0; r < K.rT; ++r)
-          acc += ldAk<F32>(K, (size_t)(tt + t) * K.rT_pad + r) *
+          acc += ldAk<F32>(K, ak_index(tt + t, r, K.rT_pad)) *
                  ldf<F32>(K.G, ((size_t)h * K.rF_pad + j) * K.rT_pad + r);
       P[t][j] = acc;
     }

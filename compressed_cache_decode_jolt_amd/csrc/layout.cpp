@@ -109,7 +109,8 @@ void stage_cache(const jolt_cache_desc *desc, Staged *S, int threads) {
       m.rT_pad = pad_rank(in.r_T);
       m.rF_pad = (in.r_F + kRankPad - 1) / kRankPad * kRankPad;
       CellOffsets &o = S->offs[2 * g + tau];
-      // A.  bf16 caches: fp16 scaled by a power of two a_s (exact for every
+      // A (keys in the ak_index layout, values in av_index).  bf16 caches:
+      // fp16 scaled by a power of two a_s (exact for every
       // bf16 value in fp16's normal range) so that the MFMA products take A
       // as it is -- A_K rows in the key tile, A_V against fp16 softmax
       // weights (11-bit, where bf16 weights would carry 8); W2 carries the
@@ -128,7 +129,7 @@ void stage_cache(const jolt_cache_desc *desc, Staged *S, int threads) {
       }
       for (int t = 0; t < T; ++t)
         for (int r = 0; r < m.rT; ++r) {
-          const size_t dst = tau == 0 ? (size_t)t * m.rT_pad + r : av_index(t, r, m.rT_pad);
+          const size_t dst = tau == 0 ? ak_index(t, r, m.rT_pad) : av_index(t, r, m.rT_pad);
           if (!f32)
             ((_Float16 *)(S->buf.data() + o.A))[dst] =
                 (_Float16)(load_factor(in.A, (size_t)t * m.rT + r, false) * (float)m.a_s);

@@ -70,6 +70,17 @@ JOLT_HD inline void kcode_pos(int h, int t, int i, int bits, int T_pad, int d, s
   *shift = sh;
 }
 
+// A_K element (t, r): one B operand of the key tile's 16x16x32 MFMA -- 16
+// tokens x 32 ranks, 1 KiB in fp16 -- per (16-token block, 32-rank step),
+// blocks outermost; lane (t & 15) * 4 + ((r >> 3) & 3) of the operand holds
+// ranks 8 ((r >> 3) & 3) .. + 7 of token t, so one wave load of a step reads
+// one contiguous KiB (8 whole cache lines, where token rows would touch 16
+// half lines).  rT_pad is a multiple of 32.
+JOLT_HD inline size_t ak_index(int t, int r, int rT_pad) {
+  return (((size_t)(t >> 4) * (rT_pad >> 5) + (r >> 5)) * 64 + (t & 15) * 4 + ((r >> 3) & 3)) * 8 +
+         (r & 7);
+}
+
 // Value-side layouts follow the operands of a 16x16x16 MFMA whose K
 // dimension is 16 tokens: lane (row & 15) * 4 + (t & 15) / 4 holds the four
 // consecutive tokens t & ~3 .. (t & ~3) + 3 of one row (a value rank or a

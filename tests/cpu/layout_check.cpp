@@ -12,7 +12,7 @@
 //   * value codes: the lane records of a 16-token block, pairs per feature
 //     block -> the same;
 //   * every bit of a code section that no read touches must be zero;
-//   * A_K rows and A_V tiles at the kernel's addresses -> fp16(A * a_s);
+//   * A_K fragments and A_V tiles at the kernel's addresses -> fp16(A * a_s);
 //   * W2[h] = B G[h]^T / a_s within fp16 rounding, padding columns zero.
 // Prints "layout check OK" and exits 0, or reports the first mismatch.
 #include <cmath>
@@ -147,7 +147,7 @@ static void run_case(int T, int H, int d, const std::vector<int> &gsz,
       // A at the kernel's addresses
       for (int t = 0; t < T; ++t)
         for (int r = 0; r < m.rT_pad; ++r) {
-          const size_t at = tau == 0 ? o.A + 2 * ((size_t)t * m.rT_pad + r)
+          const size_t at = tau == 0 ? o.A + 2 * ak_index(t, r, m.rT_pad)
                                      : o.A + 2 * av_index(t, r, m.rT_pad);
           _Float16 v;
           std::memcpy(&v, buf + at, 2);
