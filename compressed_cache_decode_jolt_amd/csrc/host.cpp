@@ -265,7 +265,7 @@ struct Plan {
   size_t tail_off;
   // one query per KV head with value ranks above 128 (key ranks up to 256):
   // the value factors in a second pass over all heads (value2.hip), with the
-  // logits [batch][H][sc_stride] at sc_off, the merge's (max, sum) at st_off
+  // logits [batch][sc_stride / 16][H][16] at sc_off, the merge's (max, sum) at st_off
   // and the partial factor sums [batch][n2split][H][rV_max] at p2_off
   bool v2;
   int sc_stride, n2split, split2;

@@ -132,8 +132,9 @@ struct MfmaArgs {
   // bitwise reproducible; 0: blocks claimed on demand
   int32_t fixed_blocks;
   // one query per KV head, value factors in a second pass (the split kernel
-  // variant with SCO): every token's logit goes to scores[(slot H + h)
-  // sc_stride + t] and the split partials carry the residual part only
+  // variant with SCO): every token's logit goes to scores, laid out
+  // [slot][sc_stride / 16][H][16] (per 16-token block, the 16 logits of every
+  // head in turn), and the split partials carry the residual part only
   float *scores;
   int32_t sc_stride;
   SeqMfma seq[kMaxBatchPerLaunch];
@@ -175,7 +176,7 @@ struct SeqV2 {
   int32_t T, rT_pad, slot, pad_;
 };
 struct V2Args {
-  const float *scores;   // logits [slot][H][sc_stride]
+  const float *scores;   // logits [slot][sc_stride / 16][H][16]
   const float *stats;    // (m*, L*) [slot][H][2] from the merge
   float *part;           // [slot][n2split][H][rV_max] partial a
   float *out;            // [slot][H][d], the merge's output, a-part added

@@ -51,12 +51,11 @@ __device__ inline float ldq(const void *q, size_t i, bool f32) {
 }
 
 __device__ inline int k_code(const CellDev &c, int h, int t, int i, int T_pad, int d) {
-  const int b = c.bits;
-  const uint8_t *row = c.codes + ((size_t)h * T_pad + t) * (d * b / 8);
-  int s = i >> 5, g = (i >> 3) & 3, j = i & 7, dw, sh;
-  code_pos(8 * s + j, b, &dw, &sh);
-  uint32_t w = *(const uint32_t *)(row + g * (d * b / 32) + 4 * dw);
-  return (w >> sh) & ((1u << b) - 1u);
+  size_t at;
+  int sh;
+  kcode_pos(h, t, i, c.bits, T_pad, d, &at, &sh);
+  const uint32_t w = *(const uint32_t *)(c.codes + at);
+  return (w >> sh) & ((1u << c.bits) - 1u);
 }
 
 __device__ inline int v_code(const CellDev &c, int h, int t, int i, int T_pad, int d) {

@@ -58,15 +58,22 @@ JOLT_HD inline void code_pos(int q, int bits, int *dword, int *shift) {
   *shift = bits * ((P % npair) + (q & 1) * npair);
 }
 
-// Key residual codes: a row of one (head, token) is d*b/8 bytes in 4 chunks
-// of d*b/32 bytes, one per 16-lane group g of the MFMA operand; chunk g holds
+// Key residual codes: a (head, token) row has d*b/8 bytes in 4 chunks of
+// d*b/32 bytes, one per 16-lane group g of the MFMA operand; chunk g holds
 // rotated feature i = 32 s + 8 g + j as slot q = 8 s + j in code_pos order.
+// Per 16-token block of a head, the lanes (t & 15, g) read their chunks as
+// pieces of at most 16 bytes; piece x of every lane sits in one contiguous
+// run of 64 pieces (lane (t & 15) * 4 + g at 16 bytes each), so a wave load
+// of a piece reads contiguous bytes.  Chunks of 16 bytes or less are one
+// piece, and the block is then simply its 16 rows in order.
 JOLT_HD inline void kcode_pos(int h, int t, int i, int bits, int T_pad, int d, size_t *byte,
                               int *shift) {
   int dw, sh;
   code_pos(8 * (i >> 5) + (i & 7), bits, &dw, &sh);
-  *byte = ((size_t)h * T_pad + t) * (size_t)(d * bits / 8) + ((i >> 3) & 3) * (size_t)(d * bits / 32) +
-          4 * (size_t)dw;
+  const int cb = d * bits / 32, pc = cb < 16 ? cb : 16;  // chunk, piece bytes
+  const int x = 4 * dw / pc, in = 4 * dw - x * pc;       // piece, byte in it
+  *byte = ((size_t)h * T_pad + (t & ~15)) * (size_t)(d * bits / 8) + (size_t)x * 64 * pc +
+          (size_t)((t & 15) * 4 + ((i >> 3) & 3)) * pc + in;
   *shift = sh;
 }
 

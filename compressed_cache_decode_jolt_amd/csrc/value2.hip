@@ -34,7 +34,12 @@ constexpr int kUB = 4;     // token blocks whose operands are loaded ahead toget
 // tokens 4 lg .. 4 lg + 3 (the B operand of a 16x16x16 product whose K
 // dimension is tokens) and the A_V fragment of rank 16 k + lr for the same
 // tokens (the A operand, as the value layout stores it); the product
-// accumulates a[rank][head] for 16 ranks x 16 heads.
+// accumulates a[rank][head] for 16 ranks x 16 heads.  The operands of kUB
+// blocks are loaded together, double-buffered: the next kUB blocks' loads go
+// out before the current ones are used, so a wave always has one batch in
+// flight while it computes the other.  Logits are stored per 16-token block
+// (all heads' 16 logits in turn), so a head group's operand is one
+// contiguous KiB.
 __global__ __launch_bounds__(64 * kWaves) void value_gemm(jolt::V2Args a) {
   const int split = blockIdx.x, si = blockIdx.y;
   const jolt::SeqV2 &sq = a.seq[si];
@@ -57,27 +62,30 @@ __global__ __launch_bounds__(64 * kWaves) void value_gemm(jolt::V2Args a) {
     for (int g = 0; g < 2; ++g) acc[j][g] = f32x4{0, 0, 0, 0};
   const int ng = H > 16 ? 2 : 1;
   const int nb = t1 > t0 ? (t1 - t0) >> 4 : 0;
-  for (int b0 = 0; b0 < nb; b0 += kUB) {
-    // the operands of kUB blocks first (blocks past the split's end re-read
-    // its last block and are not used)
-    f32x4 s4[kUB][2];
-    u32x2 fr[kUB][kRB];
+  f32x4 s4[2][kUB][2];
+  u32x2 fr[2][kUB][kRB];
+  // operands of blocks b0 .. b0 + kUB - 1 into buffer q (blocks past the
+  // split's end re-read its last block and are not used)
+  auto load = [&](int q, int b0) {
 #pragma unroll
     for (int u = 0; u < kUB; ++u) {
       const int tb = t0 + 16 * min(b0 + u, nb - 1);
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         const int head = 16 * g + lr;
-        s4[u][g] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-        if (g < ng && head < H) s4[u][g] = *(const f32x4 *)(sc + (size_t)head * a.sc_stride + tb + 4 * lg);
+        s4[q][u][g] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        if (g < ng && head < H)
+          s4[q][u][g] = *(const f32x4 *)(sc + ((size_t)(tb >> 4) * H + head) * 16 + 4 * lg);
       }
       const uint32_t avb = 2u * ((uint32_t)(tb >> 4) * nMV * 64 + vlane) * 4;
 #pragma unroll
       for (int j = 0; j < kRB; ++j) {
         const int k = wave + kWaves * j;
-        fr[u][j] = ldg<u32x2>(sq.A, avb + 512u * (uint32_t)min(k, nMV - 1));
+        fr[q][u][j] = ldg<u32x2>(sq.A, avb + 512u * (uint32_t)min(k, nMV - 1));
       }
     }
+  };
+  auto compute = [&](int q, int b0) {
 #pragma unroll
     for (int u = 0; u < kUB; ++u) {
       if (b0 + u >= nb) break;
@@ -85,13 +93,22 @@ __global__ __launch_bounds__(64 * kWaves) void value_gemm(jolt::V2Args a) {
 #pragma unroll
       for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bP[g][i] = (_Float16)__expf(s4[u][g][i] - mst[g]);
+        for (int i = 0; i < 4; ++i) bP[g][i] = (_Float16)__expf(s4[q][u][g][i] - mst[g]);
 #pragma unroll
       for (int j = 0; j < kRB; ++j) {
-        const f16x4 af = __builtin_bit_cast(f16x4, fr[u][j]);
+        const f16x4 af = __builtin_bit_cast(f16x4, fr[q][u][j]);
         acc[j][0] = __builtin_amdgcn_mfma_f32_16x16x16f16(af, bP[0], acc[j][0], 0, 0, 0);
         if (ng > 1) acc[j][1] = __builtin_amdgcn_mfma_f32_16x16x16f16(af, bP[1], acc[j][1], 0, 0, 0);
       }
+    }
+  };
+  if (nb > 0) {
+    load(0, 0);
+    for (int b0 = 0; b0 < nb; b0 += 2 * kUB) {
+      load(1, b0 + kUB);
+      compute(0, b0);
+      load(0, b0 + 2 * kUB);
+      compute(1, b0 + kUB);
     }
   }
   // lane (lr, lg) holds a[head 16 g + lr][ranks 16 k + 4 lg .. + 3]
@@ -114,48 +131,67 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
-// grid (H, nseq), 512 threads: the splits' partial a of one (sequence, head)
-// summed in LDS, then every output feature f as a wave-wide dot product of
-// W2_V row f (lane: 8 ranks) with a, four rows per wave step so that their
-// loads are in flight together, scaled by 1 / L* and added to out.
+// grid (H, nseq), 512 threads: every output feature f as a wave-wide dot
+// product of W2_V row f (lane: 8 ranks) with the splits' summed partial a of
+// one (sequence, head), scaled by 1 / L* and added to out.  Thread r first
+// loads rank r's partials of the first 16 splits, then wave w issues its 16
+// rows 4 w + 32 i + u (i, u < 4) of W2_V, so that the rows are in flight
+// while the partials (loaded first, so waited for first) are summed in LDS.
 constexpr int kFinWaves = 8;
+constexpr int kFinSplits = 16;  // splits whose partials are loaded ahead of W2_V
 __global__ __launch_bounds__(64 * kFinWaves) void value_finish(jolt::V2Args a) {
   const int h = blockIdx.x, si = blockIdx.y;
   const jolt::SeqV2 &sq = a.seq[si];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int rV = sq.rT_pad, H = a.H, d = a.d;
-  __shared__ float av[512];
-  {
-    const float *pp = a.part + ((size_t)sq.slot * a.n2split * H + h) * a.rV_max;
-    const size_t sstride = (size_t)H * a.rV_max;
-    for (int r = tid; r < rV; r += 64 * kFinWaves) {
-      float x = 0.0f;
-#pragma unroll 8
-      for (int sp = 0; sp < a.n2split; ++sp) x += pp[sp * sstride + r];
-      av[r] = x;
+  const int rV = sq.rT_pad, H = a.H, d = a.d;  // rV <= 512 = the threads, a multiple of 32
+  const float *pp = a.part + ((size_t)sq.slot * a.n2split * H + h) * a.rV_max + tid;
+  const size_t sstride = (size_t)H * a.rV_max;
+  const bool mine = tid < rV;  // this thread sums rank tid
+  float pv[kFinSplits];
+#pragma unroll
+  for (int k = 0; k < kFinSplits; ++k) pv[k] = mine && k < a.n2split ? pp[k * sstride] : 0.0f;
+  const _Float16 *W = sq.W2 + (size_t)h * d * rV;
+  const int r0 = 8 * lane;  // the lane's ranks r0 .. r0 + 7
+  const bool has = r0 < rV;
+  f16x8 w[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int f = min(4 * wave + 32 * i + u, d - 1);
+      w[i][u] = has ? *(const f16x8 *)(W + (size_t)f * rV + r0) : f16x8{};
     }
+  __shared__ float av[512];
+  if (mine) {
+    float x = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kFinSplits; ++k) x += pv[k];
+    for (int sp = kFinSplits; sp < a.n2split; ++sp) x += pp[sp * sstride];
+    av[tid] = x;
   }
   __syncthreads();
   const float inv = 1.0f / a.stats[((size_t)sq.slot * H + h) * 2 + 1];
-  const _Float16 *W = sq.W2 + (size_t)h * d * rV;
-  const int r0 = 8 * lane;
-  for (int f0 = 4 * wave; f0 < d; f0 += 4 * kFinWaves) {
-    float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int r = r0; r < rV; r += 512) {
-      f16x8 w[4];
+  float y[8];
+  if (has) {
+    const f32x4 a0 = *(const f32x4 *)(av + r0), a1 = *(const f32x4 *)(av + r0 + 4);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) w[u] = *(const f16x8 *)(W + (size_t)min(f0 + u, d - 1) * rV + r);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[u] += (float)w[u][e] * av[r + e];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float y = wave_sum(x[u]);
-      if (lane == 0 && f0 + u < d) a.out[((size_t)sq.slot * H + h) * d + f0 + u] += y * inv;
+    for (int e = 0; e < 4; ++e) {
+      y[e] = a0[e];
+      y[4 + e] = a1[e];
     }
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float x = 0.0f;
+      if (has)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x += (float)w[i][u][e] * y[e];
+      x = wave_sum(x);
+      const int f = 4 * wave + 32 * i + u;
+      if (lane == 0 && f < d) a.out[((size_t)sq.slot * H + h) * d + f] += x * inv;
+    }
 }
 
 }  // namespace

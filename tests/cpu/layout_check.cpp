@@ -189,21 +189,29 @@ static void run_case(int T, int H, int d, const std::vector<int> &gsz,
             std::memcpy(&sc, buf + o.scales[lp] + 4 * ((size_t)h * T_pad + t), 4);
             CHECK(sc == c.scales[((size_t)lp * H + h) * T + t], "scale");
             if (tau == 0) {
-              // lane group lg's chunk of the row; residual step j unpacks
-              // slots 8 j .. 8 j + 7 = features 32 j + 8 lg + e
+              // lane group lg's chunk of the row, read as the kernel reads
+              // it: chunks of 8 bytes in place in the row, wider ones as
+              // 16-byte pieces, piece x of lane (t & 15, lg) at 1024 x +
+              // 16 (4 (t & 15) + lg) from the 16-token block's first row;
+              // residual step j unpacks slots 8 j .. 8 j + 7 = features
+              // 32 j + 8 lg + e
               const int cb = d * b / 32, npair = 16 / b;
               for (int lg = 0; lg < 4; ++lg) {
-                const size_t chunk = ((size_t)h * T_pad + t) * rowb + (size_t)lg * cb;
+                auto word_at = [&](int dw) -> size_t {
+                  if (cb <= 8) return ((size_t)h * T_pad + t) * rowb + (size_t)lg * cb + 4 * dw;
+                  const size_t blk = ((size_t)h * T_pad + (t & ~15)) * rowb;
+                  return blk + 1024 * (size_t)(dw / 4) + 16 * (size_t)(4 * (t & 15) + lg) + 4 * (dw % 4);
+                };
                 for (int j = 0; j < d / 32; ++j)
                   for (int p = 0; p < 4; ++p) {
                     const int P = 4 * j + p;
                     uint32_t w;
-                    std::memcpy(&w, C + chunk + 4 * (P / npair), 4);
+                    std::memcpy(&w, C + word_at(P / npair), 4);
                     float v[2];
                     code_pair(w, b * (P % npair), b, v);
                     for (int e = 0; e < 2; ++e) {
                       const int i = 32 * j + 8 * lg + 2 * p + e;
-                      mark(chunk + 4 * (P / npair), b * (P % npair) + 16 * e);
+                      mark(word_at(P / npair), b * (P % npair) + 16 * e);
                       CHECK(v[e] == (float)canon(row, i, b) - L2 + 0.5f,
                             "K code lp%d h%d t%d i%d b%d: %g vs %d", lp, h, t, i, b, (double)v[e], canon(row, i, b));
                     }
