@@ -34,49 +34,52 @@ constexpr int kUB = 4;     // token blocks whose operands are loaded ahead toget
 // tokens 4 lg .. 4 lg + 3 (the B operand of a 16x16x16 product whose K
 // dimension is tokens) and the A_V fragment of rank 16 k + lr for the same
 // tokens (the A operand, as the value layout stores it); the product
-// accumulates a[rank][head] for 16 ranks x 16 heads.  The operands of kUB
-// blocks are loaded together, double-buffered: the next kUB blocks' loads go
-// out before the current ones are used, so a wave always has one batch in
-// flight while it computes the other.  Logits are stored per 16-token block
-// (all heads' 16 logits in turn), so a head group's operand is one
-// contiguous KiB.
+// accumulates a[rank][head] for 16 ranks x 16 heads.  Tokens go in batches of
+// kUB blocks.  The weights of a batch are evaluated once per workgroup --
+// thread (u, g, lane) turns the four logits of its operand slot into fp16
+// exp(s - m*) in an LDS tile -- and every wave reads its B operands there;
+// the tile and the waves' A_V fragments are double-buffered, so the next
+// batch's logits and fragments are in flight while the current one is
+// multiplied, with one barrier per batch.  Logits are stored per 16-token
+// block (all heads' 16 logits in turn), so the batch's logits are 8 KiB in
+// one piece.
 __global__ __launch_bounds__(64 * kWaves) void value_gemm(jolt::V2Args a) {
+  static_assert(kUB * 2 * 64 == 64 * kWaves, "one logit operand slot per thread and batch");
   const int split = blockIdx.x, si = blockIdx.y;
   const jolt::SeqV2 &sq = a.seq[si];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int H = a.H, nMV = sq.rT_pad >> 4;  // (> 0: the host sends no rank-0 value factor)
   const int T16 = (sq.T + 15) & ~15;  // the split kernel wrote logits (masked) up to here
   const int t0 = split * a.split2, t1 = min(T16, t0 + a.split2);
-  float mst[2];
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int head = 16 * g + lr;
-    mst[g] = head < H ? a.stats[((size_t)sq.slot * H + head) * 2] : 0.0f;
-  }
+  const int ng = H > 16 ? 2 : 1;
+  const int nb = t1 > t0 ? (t1 - t0) >> 4 : 0;
+  // this thread's operand slot of every batch: block su, head group sg, lane
+  // lane (head 16 sg + lr, tokens 4 lg .. 4 lg + 3)
+  const int su = tid >> 7, sg = (tid >> 6) & 1, shead = 16 * sg + lr;
+  const bool slive = sg < ng && shead < H;
+  const float smax = slive ? a.stats[((size_t)sq.slot * H + shead) * 2] : 0.0f;
   const float *sc = a.scores + (size_t)sq.slot * H * a.sc_stride;
   const uint32_t vlane = (uint32_t)lr * 4 + lg;
+  __shared__ f16x4 Pt[2][kUB][2][64];  // the weights of a batch, by (block, head group, lane)
   f32x4 acc[kRB][2];
 #pragma unroll
   for (int j = 0; j < kRB; ++j)
 #pragma unroll
     for (int g = 0; g < 2; ++g) acc[j][g] = f32x4{0, 0, 0, 0};
-  const int ng = H > 16 ? 2 : 1;
-  const int nb = t1 > t0 ? (t1 - t0) >> 4 : 0;
-  f32x4 s4[2][kUB][2];
-  u32x2 fr[2][kUB][kRB];
-  // operands of blocks b0 .. b0 + kUB - 1 into buffer q (blocks past the
-  // split's end re-read its last block and are not used)
+  f32x4 s4;                // this thread's logits of the next batch
+  u32x2 fr[2][kUB][kRB];   // the wave's A_V fragments, per buffer
+  // loads of batch b0 (blocks b0 .. b0 + kUB - 1; blocks past the split's
+  // end re-read its last block and are not used)
   auto load = [&](int q, int b0) {
+    {
+      const int tb = t0 + 16 * min(b0 + su, nb - 1);
+      s4 = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      if (slive) s4 = *(const f32x4 *)(sc + ((size_t)(tb >> 4) * H + shead) * 16 + 4 * lg);
+    }
 #pragma unroll
     for (int u = 0; u < kUB; ++u) {
       const int tb = t0 + 16 * min(b0 + u, nb - 1);
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int head = 16 * g + lr;
-        s4[q][u][g] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-        if (g < ng && head < H)
-          s4[q][u][g] = *(const f32x4 *)(sc + ((size_t)(tb >> 4) * H + head) * 16 + 4 * lg);
-      }
       const uint32_t avb = 2u * ((uint32_t)(tb >> 4) * nMV * 64 + vlane) * 4;
 #pragma unroll
       for (int j = 0; j < kRB; ++j) {
@@ -85,30 +88,39 @@ __global__ __launch_bounds__(64 * kWaves) void value_gemm(jolt::V2Args a) {
       }
     }
   };
+  auto weights = [&](int q) {
+    f16x4 p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = (_Float16)__expf(s4[i] - smax);
+    Pt[q][su][sg][lane] = p;
+  };
   auto compute = [&](int q, int b0) {
 #pragma unroll
     for (int u = 0; u < kUB; ++u) {
       if (b0 + u >= nb) break;
-      f16x4 bP[2];
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bP[g][i] = (_Float16)__expf(s4[q][u][g][i] - mst[g]);
+      const f16x4 bP0 = Pt[q][u][0][lane];
+      const f16x4 bP1 = Pt[q][u][1][lane];
 #pragma unroll
       for (int j = 0; j < kRB; ++j) {
         const f16x4 af = __builtin_bit_cast(f16x4, fr[q][u][j]);
-        acc[j][0] = __builtin_amdgcn_mfma_f32_16x16x16f16(af, bP[0], acc[j][0], 0, 0, 0);
-        if (ng > 1) acc[j][1] = __builtin_amdgcn_mfma_f32_16x16x16f16(af, bP[1], acc[j][1], 0, 0, 0);
+        acc[j][0] = __builtin_amdgcn_mfma_f32_16x16x16f16(af, bP0, acc[j][0], 0, 0, 0);
+        if (ng > 1) acc[j][1] = __builtin_amdgcn_mfma_f32_16x16x16f16(af, bP1, acc[j][1], 0, 0, 0);
       }
     }
   };
-  if (nb > 0) {
+  if (nb > 0) {  // (uniform over the workgroup)
     load(0, 0);
+    weights(0);
+    __syncthreads();
     for (int b0 = 0; b0 < nb; b0 += 2 * kUB) {
       load(1, b0 + kUB);
       compute(0, b0);
+      weights(1);
+      __syncthreads();  // tile 1 written; every wave is done with tile 0
       load(0, b0 + 2 * kUB);
       compute(1, b0 + kUB);
+      weights(0);
+      __syncthreads();
     }
   }
   // lane (lr, lg) holds a[head 16 g + lr][ranks 16 k + 4 lg .. + 3]
