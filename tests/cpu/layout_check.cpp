@@ -144,11 +144,18 @@ static void run_case(int T, int H, int d, const std::vector<int> &gsz,
       const CellMeta &m = S.cells[2 * g + tau];
       const CellOffsets &o = S.offs[2 * g + tau];
       CHECK(m.rT_pad == pad_rank(c.rT) && m.rT_pad % 32 == 0 && m.rT_pad >= c.rT, "rT_pad");
-      // A at the kernel's addresses
+      // A at the kernel's addresses.  Keys as the MFMA kernel's fetch forms
+      // them: lane (lr, lg) of the 16 tokens from tb reads, for 32-rank step
+      // ks, the 16 bytes at tb 64 KT + 1024 ks + 16 (4 lr + lg), element j
+      // being rank 32 ks + 8 lg + j of token tb + lr (KT = rT_pad / 32).
+      auto ak_fetch = [&](int t, int r) -> size_t {
+        const int KT = m.rT_pad / 32, tb = t & ~15, lr = t & 15, ks = r / 32, lg = (r / 8) & 3,
+                  j = r & 7;
+        return (size_t)tb * 64 * KT + 1024 * (size_t)ks + 16 * (size_t)(4 * lr + lg) + 2 * (size_t)j;
+      };
       for (int t = 0; t < T; ++t)
         for (int r = 0; r < m.rT_pad; ++r) {
-          const size_t at = tau == 0 ? o.A + 2 * ak_index(t, r, m.rT_pad)
-                                     : o.A + 2 * av_index(t, r, m.rT_pad);
+          const size_t at = tau == 0 ? o.A + ak_fetch(t, r) : o.A + 2 * av_index(t, r, m.rT_pad);
           _Float16 v;
           std::memcpy(&v, buf + at, 2);
           const float want = r < c.rT ? (float)(_Float16)(bf16f(c.A[(size_t)t * c.rT + r]) * (float)m.a_s) : 0.0f;
