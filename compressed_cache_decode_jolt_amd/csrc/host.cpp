@@ -533,6 +533,7 @@ static jolt_status decode_impl(const jolt_cache *const *caches, int32_t batch, i
   a.rV_max = p.rV_max;
   const size_t qbytes = (size_t)c0->H_q * c0->d * (a.q_f32 ? 4 : 2);
   const bool mfma = p.kernel == JOLT_KERNEL_MFMA;
+  const bool direct = mfma && p.n_split == 1 && p.n_tsplit == 0;  // nothing to merge
   // splits per workspace row: the MFMA path keeps the tail's partials in the
   // same rows, after the split kernel's
   const int ws_splits = mfma ? p.n_split + p.n_tsplit : p.n_split;
@@ -584,6 +585,10 @@ static jolt_status decode_impl(const jolt_cache *const *caches, int32_t batch, i
       ma.split_tokens = a.split_tokens;
       ma.stride = a.stride;
       ma.fixed_blocks = launch && launch->deterministic ? 1 : 0;
+      // one split and no tail: the split kernel writes the output (and the
+      // second value pass's statistics) itself, and no merge runs
+      ma.out = direct ? a.out : nullptr;
+      ma.stats = direct && p.v2 ? (float *)v2.stats : nullptr;
       bool done[kMaxBatchPerLaunch] = {};
       int last_class = 0;  // first member of the chunk's last launch class
       for (int i0 = 0; i0 < nb; ++i0) {
@@ -713,9 +718,11 @@ static jolt_status decode_impl(const jolt_cache *const *caches, int32_t batch, i
       if (e != hipSuccess) return fail(JOLT_E_HIP, "tail kernel launch: %s", hipGetErrorString(e));
     }
     a.nseq = nb;
-    e = mfma ? jolt_launch_merge_outputs(a, nb, ws_splits, s, p.v2 ? (float *)v2.stats : nullptr)
-             : jolt_launch_merge(a, nb, s);
-    if (e != hipSuccess) return fail(JOLT_E_HIP, "merge kernel launch: %s", hipGetErrorString(e));
+    if (!direct) {
+      e = mfma ? jolt_launch_merge_outputs(a, nb, ws_splits, s, p.v2 ? (float *)v2.stats : nullptr)
+               : jolt_launch_merge(a, nb, s);
+      if (e != hipSuccess) return fail(JOLT_E_HIP, "merge kernel launch: %s", hipGetErrorString(e));
+    }
     if (p.v2) {
       e = jolt_launch_value2(v2, s, ev_last);
       if (e != hipSuccess) return fail(JOLT_E_HIP, "value pass launch: %s", hipGetErrorString(e));

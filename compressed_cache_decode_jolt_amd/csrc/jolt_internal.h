@@ -137,6 +137,12 @@ struct MfmaArgs {
   // head in turn), and the split partials carry the residual part only
   float *scores;
   int32_t sc_stride;
+  // one split per (sequence, KV head) and no tail (nothing to merge): when
+  // out is set, the kernel writes each query head's output o / l to
+  // out[(slot H_q + query head) d + f] instead of a partial, and, when stats
+  // is set, its (max, weight sum) to stats[(slot H_q + query head) 2 + 0/1]
+  float *out;
+  float *stats;
   SeqMfma seq[kMaxBatchPerLaunch];
 };
 static_assert(sizeof(MfmaArgs) <= 4096, "MFMA kernel arguments exceed 4 KiB");

@@ -7,8 +7,9 @@ Against the oracle's decode of the same caches, at the MFMA tolerances
 
 * one launch class whose sequences have different value ranks, one of them
   0 (no value factor: the second pass skips it) and ragged lengths, with
-  short splits and with splits of 1024 tokens (two 16-token blocks per wave
-  step in the split kernel);
+  short splits, with splits of 1024 tokens (two 16-token blocks per wave
+  step in the split kernel) and with one split per sequence (the split
+  kernel then writes the output and the statistics itself, no merge);
 * more than 32 sequences (two batch chunks: the logits, statistics and
   partial sums at the second chunk's offsets);
 * an uncompressed tail under the same softmax;
@@ -68,7 +69,7 @@ def check(got, caches, q, q_pos, inv, scale):
         assert r <= 5e-3 and mx <= 2e-2, (b, r, mx)
 
 
-@pytest.mark.parametrize("split", [0, 1024])
+@pytest.mark.parametrize("split", [0, 1024, 2048])
 def test_class_with_mixed_value_ranks(split):
     d, H = 128, 4
     # same key bits, key rank and value bits: one launch class; value ranks
