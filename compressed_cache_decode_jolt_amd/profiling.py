@@ -73,20 +73,31 @@ def window_mean(trace, match, start, count):
 
 
 def call_window_mean(trace, start, count, first="decode_mfma", last="value_finish",
-                     kernels=("decode_mfma", "merge_outputs", "value_gemm", "value_finish")):
+                     kernels=("decode_mfma", "merge_outputs", "value_gemm", "value_finish"),
+                     per_call=None):
     """Mean span (us) of layer calls start .. start+count-1 of a --kernel-trace
     CSV: a call is a run of ``first`` dispatches and the kernels after it up
     to the next ``first``; its span runs from its first dispatch's start to
     the end of its ``last`` dispatch if it has one, else of its last
-    ``first`` dispatch -- what the library's timing events bracket."""
+    ``first`` dispatch -- what the library's timing events bracket.  A call
+    launches each of its classes (kernel names) once, so a ``first``
+    dispatch whose name the current run already holds starts a new call
+    (single-split calls without a value pass have no kernel in between).
+    per_call: the calls' number of ``first`` dispatches where it is fixed
+    (a call of one class, e.g.), so that calls of different classes that
+    follow each other with nothing in between are told apart too."""
     rows = [r for r in csv.DictReader(open(trace)) if any(k in r["Kernel_Name"] for k in kernels)]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    calls, cur, prev_first = [], None, False
+    calls, cur, prev_first, seen = [], None, False, set()
     for r in rows:
         is_first = first in r["Kernel_Name"]
-        if is_first and not prev_first:
+        if is_first and (not prev_first or r["Kernel_Name"] in seen or
+                         (per_call and len(seen) >= per_call)):
             cur = {"start": int(r["Start_Timestamp"]), "end_first": 0, "end_last": None}
             calls.append(cur)
+            seen = set()
+        if is_first:
+            seen.add(r["Kernel_Name"])
         if cur is None:
             continue
         if is_first:
@@ -227,6 +238,8 @@ def main():
     s.add_argument("--call-window", nargs=2, type=int, metavar=("START", "COUNT"), default=None,
                    help="also report the mean span of these layer calls (split kernels to "
                         "the end of the second value pass)")
+    s.add_argument("--call-dispatches", type=int, default=None,
+                   help="split-kernel dispatches per layer call, where it is fixed")
     t = sub.add_parser("traffic")
     for k in ("workload", "kernel", "fetch", "write", "calib_fetch", "calib_write", "out"):
         t.add_argument("--" + k.replace("_", "-"), required=True)
@@ -259,7 +272,7 @@ def main():
             st, n = a.call_window
             text += ("\nMean span of layer calls %d-%d (first split-kernel start to the end of the "
                      "call's last split kernel, or of its second value pass): %.2f us\n"
-                     % (st, st + n - 1, call_window_mean(a.trace, st, n)))
+                     % (st, st + n - 1, call_window_mean(a.trace, st, n, per_call=a.call_dispatches)))
         text += "\nKernel sources hash: `%s`\n" % kernel_hash()
         open(a.out, "w").write(text)
         print(text)

@@ -89,6 +89,25 @@ def test_call_window_spans_split_kernels_and_the_value_pass(tmp_path):
     assert P.call_window_mean(p, 1, 1) == pytest.approx(40e-3)
 
 
+def test_call_window_splits_back_to_back_calls_of_one_class(tmp_path):
+    # single-split calls write their output in the split kernel: three calls
+    # of one class with nothing in between, then a call with two classes
+    rows = [("decode_mfma<a>", 100, 140), ("decode_mfma<a>", 150, 180), ("decode_mfma<a>", 190, 200),
+            ("decode_mfma<a>", 300, 320), ("decode_mfma<b>", 320, 360), ("merge_outputs", 360, 370)]
+    p = _write(tmp_path / "trace.csv", ["Kernel_Name", "Start_Timestamp", "End_Timestamp"], rows)
+    # spans: 40, 30, 10, 360 - 300 ns
+    assert P.call_window_mean(p, 0, 4) == pytest.approx((40 + 30 + 10 + 60) / 4 / 1e3)
+    assert P.call_window_mean(p, 3, 1) == pytest.approx(60e-3)
+
+
+def test_call_window_with_one_dispatch_per_call(tmp_path):
+    # one-class calls of different classes back to back, nothing in between
+    rows = [("decode_mfma<a>", 100, 140), ("decode_mfma<b>", 150, 180), ("value_gemm", 180, 190),
+            ("value_finish", 190, 195), ("decode_mfma<c>", 200, 260)]
+    p = _write(tmp_path / "trace.csv", ["Kernel_Name", "Start_Timestamp", "End_Timestamp"], rows)
+    assert P.call_window_mean(p, 0, 3, per_call=1) == pytest.approx((40 + 45 + 60) / 3 / 1e3)
+
+
 def test_traffic_per_launch_counts_every_kernel_of_a_call(tmp_path):
     hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
     cf = _write(tmp_path / "cf.csv", hdr, [(1, "copy", "FETCH_SIZE", 1024)])
