@@ -112,7 +112,7 @@ void stage_cache(const jolt_cache_desc *desc, Staged *S, int threads) {
       // A (keys in the ak_index layout, values in av_index).  bf16 caches:
       // fp16 scaled by a power of two a_s (exact for every
       // bf16 value in fp16's normal range) so that the MFMA products take A
-      // as it is -- A_K rows in the key tile, A_V against fp16 softmax
+      // as it is -- A_K fragments in the key tile, A_V against fp16 softmax
       // weights (11-bit, where bf16 weights would carry 8); W2 carries the
       // 1 / a_s.
       o.A = S->take((size_t)fb * T_pad * std::max(m.rT_pad, 1));
